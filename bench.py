@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the OScaR INT2 KV cache on one MI355X.
+
+Workload: one Llama-3.1-8B-shaped attention layer at 128K context (batch 1,
+32 query heads, 8 KV heads, head_dim 128, 131072 cached tokens, empty bf16
+tail), seeded synthetic keys/values with channel outliers, lognormal token
+norms and an attention sink.  A step is one decode step of the INT2 path
+(rotate q, stream the packed cache, online softmax, split-K merge), the
+cache having been quantized by the library beforehand.
+
+Printed: one JSON line with the metric (achieved HBM GB/s of the decode
+step from algorithmic bytes), us/step, the roofline record of the decode
+kernel, the bf16 flash-decoding kernel on identical K/V (speed-up), the
+quantizer's throughput and the CPU oracle timed on a bounded sample.
+
+The timed region cycles through several copies of the cache placed at
+different addresses, so that the 256 MB last-level cache cannot hold the
+data being read.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "INT2-KV decode attention: achieved HBM GB/s (% of peak) and µs/step at 128K ctx"
+HBM_PEAK_GBS = 8000.0
+BYTES_PER_TOKEN_HEAD = 74          # 32 K codes + 32 V codes + 2 norm + 4 V (s,z) + 512/128 K (s,z)
+BF16_BYTES_PER_TOKEN_HEAD = 512
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--copies", type=int, default=16, help="distinct INT2 cache copies cycled through")
+    p.add_argument("--bf16-copies", type=int, default=4)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target seconds of oracle work")
+    p.add_argument("--profile", choices=["none", "int2", "bf16", "quantize", "copy"], default="none",
+                   help="run only one kernel (for rocprofv3 runs) and print its timing")
+    return p.parse_args()
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_int2_fwht_amd", "csrc")
+    for name in ("decode_int2.hip", "decode_common.hpp", "device_common.hpp", "internal.hpp"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(launch_bytes):
+    """HBM traffic of the decode kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "decode_int2_128k_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha") != kernel_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(target_s):
+    """The oracle (numpy float64, unmodified) on one KV-head slice of the
+    128K workload: quantize once (untimed), then repeated decode steps."""
+    import numpy as np
+    import oracle
+    import synthetic as syn
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    w = syn.workload(3)
+    k = syn.bf16_bits_to_f64(syn.keys_slice(w, 0, 0))
+    v = syn.bf16_bits_to_f64(syn.values_slice(w, 0, 0))
+    s = oracle.quantize_slice(k, v, 131072)
+    del k, v
+    q = syn.bf16_bits_to_f64(syn.query(w, 0)[:4])
+    sm = 1.0 / np.sqrt(128.0)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        s.decode(q, sm)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    bytes_per_rep = 131072 * BYTES_PER_TOKEN_HEAD + 4 * 128 * 2 + 4 * 128 * 4
+    return {"value": round(bytes_per_rep * reps / el / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"oracle decode of 1 of 8 KV heads (4 query heads) over 131072 quantized tokens, "
+                      f"{reps} repetitions in {el:.1f} s; GB/s = algorithmic bytes of those steps / time"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on one GPU only; multi-GPU runs are not supported "
+              "(the decode shards by KV head, sequence or batch without a collective on the hot path)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synthetic as syn
+    from kv_cache_int2_fwht_amd import binding as ob
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = syn.workload(3)
+    B, H, Hq, T = w.batch, w.num_kv_heads, w.num_q_heads, w.lengths[0]
+    sm = 1.0 / np.sqrt(128.0)
+    stream = torch.cuda.current_stream()
+
+    # ---- inputs: synthetic bf16 K/V of the 128K layer, resident in HBM ----
+    t_gen = time.perf_counter()
+    k_src = torch.empty((B, H, T, 128), dtype=torch.bfloat16, device=dev)
+    v_src = torch.empty((B, H, T, 128), dtype=torch.bfloat16, device=dev)
+    for h in range(H):
+        k_src[0, h] = torch.from_numpy(syn.keys_slice(w, 0, h).view(np.int16)).to(dev).view(torch.bfloat16)
+        v_src[0, h] = torch.from_numpy(syn.values_slice(w, 0, h).view(np.int16)).to(dev).view(torch.bfloat16)
+    q = torch.from_numpy(syn.query(w, 0).view(np.int16)).to(dev).view(torch.bfloat16)[None].contiguous()
+    gen_s = time.perf_counter() - t_gen
+
+    zeros = torch.zeros(B, dtype=torch.int32, device=dev)
+    ngroups = torch.full((B,), T // 128, dtype=torch.int32, device=dev)
+    nq = torch.full((B,), T, dtype=torch.int32, device=dev)
+    nt = torch.zeros(B, dtype=torch.int32, device=dev)
+    seq = torch.full((B,), T, dtype=torch.int32, device=dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    ws = ob.alloc_workspace(B, H, Hq, T, device=dev)
+
+    def quantize_into(cache):
+        ob.quantize_kv(cache, k_src, v_src, zeros, ngroups, T // 128)
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3   # us per call
+
+    if args.profile == "copy":
+        # plain copy kernel of known size, for calibrating the HBM byte counters
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "copy", "bytes_read": src.numel(), "bytes_written": dst.numel()}))
+        return
+
+    caches = [ob.PackedCache(B, H, T, device=dev) for _ in range(max(1, args.copies))]
+    quantize_into(caches[0])
+    torch.cuda.synchronize()
+    quant_us = timed(lambda i: quantize_into(caches[0]), 3 if args.profile == "none" else 1)
+    for c in caches[1:]:
+        for name in ("k_codes", "k_sz", "k_norm", "v_codes", "v_sz"):
+            getattr(c, name).copy_(getattr(caches[0], name))
+    torch.cuda.synchronize()
+    if args.profile == "quantize":
+        print(json.dumps({"profile": "quantize", "us_per_call": quant_us}))
+        return
+
+    def int2_step(i):
+        ob.decode_attn(caches[i % len(caches)], nq, nt, T, q, sm, out, ws, stream=stream)
+
+    int2_bytes = B * H * T * BYTES_PER_TOKEN_HEAD + B * Hq * 128 * (2 + 4)
+    for i in range(args.warmup):
+        int2_step(i)
+    torch.cuda.synchronize()
+    int2_us = timed(int2_step, args.steps)
+    if args.profile == "int2":
+        print(json.dumps({"profile": "int2", "us_per_step": int2_us}))
+        return
+
+    # ---- bf16 flash-decoding on identical unquantized K/V ----
+    kv_copies = [(k_src, v_src)] + [(k_src.clone(), v_src.clone()) for _ in range(max(0, args.bf16_copies - 1))]
+
+    def bf16_step(i):
+        kk, vv = kv_copies[i % len(kv_copies)]
+        ob.decode_attn_bf16(kk, vv, seq, T, q, sm, out, ws, stream=stream)
+
+    bf16_bytes = B * H * T * BF16_BYTES_PER_TOKEN_HEAD + B * Hq * 128 * (2 + 4)
+    for i in range(max(3, args.warmup // 4)):
+        bf16_step(i)
+    bf16_us = timed(bf16_step, max(10, args.steps // 4))
+    if args.profile == "bf16":
+        print(json.dumps({"profile": "bf16", "us_per_step": bf16_us}))
+        return
+
+    achieved = int2_bytes / (int2_us * 1e-6) / 1e9
+    traffic = traffic_record(int2_bytes)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
+    quant_bytes = B * H * T * (BF16_BYTES_PER_TOKEN_HEAD + BYTES_PER_TOKEN_HEAD)
+    rec = {
+        "metric": METRIC,
+        "value": round(achieved, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(int2_us / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "llama31-8b-layer-128k", "batch": B, "q_heads": Hq, "kv_heads": H,
+                   "head_dim": 128, "context": T, "tail": 0, "cache_copies": len(caches)},
+        "us_per_step": round(int2_us, 3),
+        "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(B / (int2_us * 1e-6), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_int2_kernel<4>", "algorithmic_bytes_per_launch": int2_bytes},
+        "bf16_reference": {"us_per_step": round(bf16_us, 3),
+                           "achieved_GBs": round(bf16_bytes / (bf16_us * 1e-6) / 1e9, 2),
+                           "algorithmic_bytes_per_launch": bf16_bytes},
+        "speedup_vs_bf16": round(bf16_us / int2_us, 3),
+        "cache_bytes_ratio_bf16_over_int2": round(BF16_BYTES_PER_TOKEN_HEAD / BYTES_PER_TOKEN_HEAD, 3),
+        "quantize_prefill": {"us": round(quant_us, 2), "GBs": round(quant_bytes / (quant_us * 1e-6) / 1e9, 2)},
+        "input_generation_s": round(gen_s, 2),
+        "kernel_sha": kernel_sha(),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

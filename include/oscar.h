@@ -1,0 +1,208 @@
+/*
+ * oscar.h -- C ABI of the OScaR INT2 KV-cache library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The library implements two things:
+ *
+ *  1. The OScaR key/value quantizer.  Each key is rotated by the orthonormal
+ *     128-point Hadamard matrix ("Canalized Rotation"), divided by its own L2
+ *     norm, which is kept in fp16 ("Omni-Token Scaling"), and quantized to
+ *     INT2 per channel over groups of 128 tokens.  Values are quantized to
+ *     INT2 per token.  Sources: OScaR abstract (arXiv 2605.19660, fugumt.com
+ *     record, "Abstract"); ai-papers.net OScaR summary, section
+ *     "OScaRの提案手法" and Fig. 4.
+ *  2. Single-query grouped-query attention over the packed cache (one decode
+ *     step), the operation whose speed-up over bf16 flash-decoding the pages
+ *     report (ai-papers.net summary, section "実験結果"; abstract), plus a bf16
+ *     flash-decoding kernel over unquantized keys/values that serves as the
+ *     speed-up denominator.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All buffers are device memory owned by the caller; the library never
+ *    allocates, frees or synchronizes.  Every compute call is asynchronous on
+ *    the given stream (a hipStream_t passed as void*; NULL = default stream).
+ *  - Host-side arguments are validated before anything is launched.  A
+ *    failing call launches nothing, returns a non-zero oscar_status and
+ *    records a message retrievable with oscar_last_error() on the same host
+ *    thread.  Nothing throws across this boundary.
+ *  - Values that live in device memory (lengths, group starts) are
+ *    preconditions stated per call; kernels skip work that would fall
+ *    outside the buffers described by oscar_kv_cache instead of faulting.
+ *  - fp16 and bf16 numbers are passed as uint16_t bit patterns.
+ *  - head_dim and the quantization group are both fixed at 128.
+ *
+ * Packed cache layout (per sequence b and KV head h; the pages fix only
+ * "INT2", the byte layout is this library's):
+ *  - 2-bit codes, four per byte, least significant bits first:
+ *    byte = c0 | c1 << 2 | c2 << 4 | c3 << 6.
+ *  - k_codes : uint8 [batch][num_kv_heads][capacity][32]; byte i of a token
+ *              row holds channels 4i..4i+3 of the rotated, scaled key.
+ *  - k_sz    : fp16 [batch][num_kv_heads][capacity/128][128][2]; per group
+ *              and channel the pair (scale s, zero-point z).
+ *  - k_norm  : fp16 [batch][num_kv_heads][capacity]; per-token L2 norm.
+ *  - v_codes : uint8 [batch][num_kv_heads][capacity/128][128][32]; per
+ *              group, one 32-byte row per channel, byte j holds tokens
+ *              4j..4j+3 of the group.
+ *  - v_sz    : fp16 [batch][num_kv_heads][capacity][2]; per token (s, z).
+ *  - k_tail, v_tail : bf16 [batch][num_kv_heads][128][128]; the tokens of
+ *              the current, not yet complete group (at most 127 are read).
+ *  Dequantization: key (rotated domain) = n * (s * c + z) with the group's
+ *  (s, z) for that channel; value = s * c + z with the token's (s, z).
+ *  All pointers must be 16-byte aligned.
+ */
+#ifndef OSCAR_H
+#define OSCAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OSCAR_ABI_VERSION 1
+#define OSCAR_HEAD_DIM 128
+#define OSCAR_GROUP 128
+
+typedef enum oscar_status {
+  OSCAR_OK = 0,
+  OSCAR_EINVAL = 1,        /* null/misaligned pointer, negative or zero size, bad stride */
+  OSCAR_EUNSUPPORTED = 2,  /* head_dim or group != 128, Hq not a multiple of Hkv, GQA ratio > 8 */
+  OSCAR_EWORKSPACE = 3,    /* workspace smaller than oscar_decode_workspace_bytes() */
+  OSCAR_EHIP = 4           /* no usable device, or the HIP launch failed */
+} oscar_status;
+
+/* Caller-owned packed cache (see the layout above). */
+typedef struct oscar_kv_cache {
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t head_dim;        /* must be 128 */
+  int32_t group;           /* must be 128 */
+  int32_t capacity;        /* tokens per sequence; a positive multiple of 128 */
+  uint8_t* k_codes;
+  uint16_t* k_sz;
+  uint16_t* k_norm;
+  uint8_t* v_codes;
+  uint16_t* v_sz;
+  const uint16_t* k_tail;  /* read by oscar_decode_attn only; may be NULL if no tail is ever used */
+  const uint16_t* v_tail;
+} oscar_kv_cache;
+
+/* Version of this ABI (OSCAR_ABI_VERSION). */
+int32_t oscar_abi_version(void);
+
+/* Static text of a status code. */
+const char* oscar_status_string(oscar_status status);
+
+/* Message of the last failing call made on this host thread ("" if none). */
+const char* oscar_last_error(void);
+
+/*
+ * oscar_quantize_kv -- prefill and group append.
+ *
+ * Quantizes whole 128-token groups of bf16 keys and values into the packed
+ * cache (OScaR abstract; ai-papers.net summary, "OScaRの提案手法"): for keys,
+ * Hadamard rotation, per-token L2 norm stored in fp16, division by that
+ * stored norm, per-channel INT2 over the group; for values, per-token INT2.
+ * INT2 is asymmetric: s = (max - min) / 3 and z = min, both stored in fp16
+ * (round to nearest even, saturating at +-65504), code =
+ * clamp(round_half_even((x - z) / s), 0, 3), code 0 where s == 0; a key
+ * whose stored norm is 0 is scaled to 0.  The rotation, norm, scaling,
+ * min/max and the division deciding each code are evaluated in fp64.
+ *
+ * k_src, v_src : bf16 sources; element (b, h, t, d) at
+ *                src + b*src_stride_b + h*src_stride_h + t*src_stride_t + d
+ *                (strides in elements, channels contiguous).  Source token
+ *                t belongs to source group t / 128.
+ * dst_group_start : device int32[batch]; source group j of sequence b is
+ *                written to cache group dst_group_start[b] + j.
+ * num_groups   : device int32[batch]; number of source groups of sequence b
+ *                to quantize (0 allowed).  Groups whose destination falls
+ *                outside [0, capacity/128) are skipped.
+ * max_groups   : host upper bound of num_groups[] (sizes the grid); 0 is a
+ *                no-op.
+ * Group append: pass the tail buffer as source (strides 128*128*Hkv,
+ * 128*128, 128), dst_group_start = n_quant / 128 and num_groups = 1 for the
+ * sequences whose tail is full, 0 otherwise.
+ */
+oscar_status oscar_quantize_kv(const oscar_kv_cache* cache,
+                               const uint16_t* k_src, const uint16_t* v_src,
+                               int64_t src_stride_b, int64_t src_stride_h,
+                               int64_t src_stride_t,
+                               const int32_t* dst_group_start,
+                               const int32_t* num_groups, int32_t max_groups,
+                               void* stream);
+
+/*
+ * Bytes of workspace that oscar_decode_attn / oscar_decode_attn_bf16 need
+ * for this shape: split-K partial softmax states (m, l, acc[128]) per query
+ * head and split, plus one arrival counter per (sequence, KV head).
+ * Returns 0 for invalid shapes.
+ */
+size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_kv_heads,
+                                    int32_t num_q_heads, int32_t max_tokens);
+
+/*
+ * Zero the arrival counters of a workspace (a fill kernel, no hipMemset).
+ * A workspace must be zero when first used; every decode call leaves its
+ * counters at zero again, so this is needed once per allocation (a buffer
+ * from a zero-filling allocator needs no call).  Calls that share one
+ * workspace must be ordered on one stream.
+ */
+oscar_status oscar_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * oscar_decode_attn -- one decode step over the packed INT2 cache.
+ *
+ * For every sequence b and query head j (KV head j / (num_q_heads /
+ * num_kv_heads)): rotate q by the same Hadamard matrix, score each quantized
+ * token as sm_scale * n * (Hq . (s * c + z)), score each tail token as
+ * sm_scale * (q . k_tail), take the softmax over all n_quant[b] + n_tail[b]
+ * tokens and write out = sum_t p_t * value_t (values dequantized as
+ * s * c + z, tail values as stored).  The token range is split across
+ * workgroups and the partial softmax states are merged in a fixed order, so
+ * results are deterministic.  An empty sequence gives out = 0.
+ *
+ * n_quant      : device int32[batch]; quantized tokens, a multiple of 128,
+ *                <= capacity (precondition).
+ * n_tail       : device int32[batch]; tail tokens, 0..127 (precondition).
+ * max_tokens   : host upper bound of n_quant[b] + n_tail[b]; sizes the grid
+ *                and the workspace.  Tokens beyond it are not read.
+ * q            : bf16 [batch][num_q_heads][128].
+ * sm_scale     : logit scale (usually 1/sqrt(128)).
+ * out          : fp32 [batch][num_q_heads][128].
+ * ws, ws_bytes : workspace of at least oscar_decode_workspace_bytes(batch,
+ *                num_kv_heads, num_q_heads, max_tokens) bytes, counters
+ *                zero (see oscar_workspace_init).  Calls that share a
+ *                workspace must not overlap.
+ */
+oscar_status oscar_decode_attn(const oscar_kv_cache* cache,
+                               const int32_t* n_quant, const int32_t* n_tail,
+                               int32_t max_tokens, const uint16_t* q,
+                               int32_t num_q_heads, float sm_scale, float* out,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * oscar_decode_attn_bf16 -- the same decode step over unquantized bf16
+ * keys and values: plain split-K flash-decoding, the counterpart of the
+ * BF16 FlashDecoding-v2 baseline the pages compare against.
+ *
+ * k, v    : bf16 [batch][num_kv_heads][capacity][128].
+ * seq_len : device int32[batch]; tokens of sequence b, <= capacity
+ *           (precondition).
+ * Other arguments as in oscar_decode_attn.
+ */
+oscar_status oscar_decode_attn_bf16(const uint16_t* k, const uint16_t* v,
+                                    int32_t batch, int32_t num_kv_heads,
+                                    int32_t capacity, const int32_t* seq_len,
+                                    int32_t max_tokens, const uint16_t* q,
+                                    int32_t num_q_heads, float sm_scale,
+                                    float* out, void* ws, size_t ws_bytes,
+                                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSCAR_H */

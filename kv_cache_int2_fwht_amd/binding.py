@@ -1,0 +1,232 @@
+"""ctypes binding of the C ABI in ``include/oscar.h`` (argument marshalling only).
+
+Every function here has the same name as its C entry point without the
+``oscar_`` prefix.  Tensors are torch tensors on the GPU; this module checks
+dtypes, shapes, contiguity and devices, turns them into pointers and passes
+torch's current stream.  All computation happens in the HIP library; if the
+library is missing this module raises instead of computing anything itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HEAD_DIM = 128
+GROUP = 128
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "liboscar.so")
+_lib = None
+
+OSCAR_OK, OSCAR_EINVAL, OSCAR_EUNSUPPORTED, OSCAR_EWORKSPACE, OSCAR_EHIP = range(5)
+
+
+class OscarError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"oscar status {status}: {message}")
+        self.status = status
+
+
+class KVCacheDesc(ctypes.Structure):
+    """Mirror of ``struct oscar_kv_cache``."""
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("capacity", ctypes.c_int32),
+        ("k_codes", ctypes.c_void_p),
+        ("k_sz", ctypes.c_void_p),
+        ("k_norm", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p),
+        ("v_sz", ctypes.c_void_p),
+        ("k_tail", ctypes.c_void_p),
+        ("v_tail", ctypes.c_void_p),
+    ]
+
+
+EXPORTED = (
+    "oscar_abi_version", "oscar_status_string", "oscar_last_error",
+    "oscar_quantize_kv", "oscar_decode_workspace_bytes", "oscar_workspace_init",
+    "oscar_decode_attn", "oscar_decode_attn_bf16",
+)
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {_LIB_PATH} is missing "
+                           "(run __graft_entry__.build())")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    L.oscar_abi_version.restype = i32
+    L.oscar_abi_version.argtypes = []
+    L.oscar_status_string.restype = ctypes.c_char_p
+    L.oscar_status_string.argtypes = [ctypes.c_int]
+    L.oscar_last_error.restype = ctypes.c_char_p
+    L.oscar_last_error.argtypes = []
+    L.oscar_quantize_kv.restype = ctypes.c_int
+    L.oscar_quantize_kv.argtypes = [ctypes.POINTER(KVCacheDesc), vp, vp, i64, i64, i64, vp, vp, i32, vp]
+    L.oscar_decode_workspace_bytes.restype = sz
+    L.oscar_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.oscar_workspace_init.restype = ctypes.c_int
+    L.oscar_workspace_init.argtypes = [vp, sz, vp]
+    L.oscar_decode_attn.restype = ctypes.c_int
+    L.oscar_decode_attn.argtypes = [ctypes.POINTER(KVCacheDesc), vp, vp, i32, vp, i32, f32, vp, vp, sz, vp]
+    L.oscar_decode_attn_bf16.restype = ctypes.c_int
+    L.oscar_decode_attn_bf16.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz, vp]
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != OSCAR_OK:
+        msg = lib().oscar_last_error().decode(errors="replace")
+        raise OscarError(status, msg)
+
+
+def _stream(stream: Optional[torch.cuda.Stream]) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor], dtype, name: str) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def abi_version() -> int:
+    return lib().oscar_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib().oscar_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().oscar_last_error().decode(errors="replace")
+
+
+class PackedCache:
+    """Caller-owned packed cache buffers (torch tensors) and their descriptor.
+
+    Shapes (B = batch, H = KV heads, C = capacity):
+      k_codes uint8 [B,H,C,32]      k_sz int16 [B,H,C/128,128,2] (fp16 bits)
+      k_norm int16 [B,H,C] (fp16)   v_codes uint8 [B,H,C/128,128,32]
+      v_sz int16 [B,H,C,2] (fp16)   k_tail / v_tail bf16 [B,H,128,128]
+    fp16 data is held in int16 tensors so that the bit patterns are exact.
+    """
+
+    def __init__(self, batch: int, num_kv_heads: int, capacity: int, device="cuda"):
+        if capacity % GROUP:
+            raise ValueError("capacity must be a multiple of 128")
+        B, H, C = batch, num_kv_heads, capacity
+        dev = torch.device(device)
+        self.batch, self.num_kv_heads, self.capacity = B, H, C
+        self.k_codes = torch.zeros((B, H, C, 32), dtype=torch.uint8, device=dev)
+        self.k_sz = torch.zeros((B, H, C // GROUP, HEAD_DIM, 2), dtype=torch.int16, device=dev)
+        self.k_norm = torch.zeros((B, H, C), dtype=torch.int16, device=dev)
+        self.v_codes = torch.zeros((B, H, C // GROUP, HEAD_DIM, 32), dtype=torch.uint8, device=dev)
+        self.v_sz = torch.zeros((B, H, C, 2), dtype=torch.int16, device=dev)
+        self.k_tail = torch.zeros((B, H, GROUP, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.v_tail = torch.zeros((B, H, GROUP, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+
+    def desc(self) -> KVCacheDesc:
+        return KVCacheDesc(
+            self.batch, self.num_kv_heads, HEAD_DIM, GROUP, self.capacity,
+            _ptr(self.k_codes, torch.uint8, "k_codes"), _ptr(self.k_sz, torch.int16, "k_sz"),
+            _ptr(self.k_norm, torch.int16, "k_norm"), _ptr(self.v_codes, torch.uint8, "v_codes"),
+            _ptr(self.v_sz, torch.int16, "v_sz"), _ptr(self.k_tail, torch.bfloat16, "k_tail"),
+            _ptr(self.v_tail, torch.bfloat16, "v_tail"))
+
+    def nbytes_packed(self) -> int:
+        """Bytes of the packed representation (codes, scales, zero-points, norms)."""
+        return sum(t.numel() * t.element_size() for t in
+                   (self.k_codes, self.k_sz, self.k_norm, self.v_codes, self.v_sz))
+
+
+def quantize_kv(cache: PackedCache, k_src: torch.Tensor, v_src: torch.Tensor,
+                dst_group_start: torch.Tensor, num_groups: torch.Tensor, max_groups: int,
+                stream: Optional[torch.cuda.Stream] = None) -> None:
+    """oscar_quantize_kv.  k_src / v_src: bf16 [B, H, T, 128] views with unit
+    channel stride (other strides arbitrary multiples of 8)."""
+    for name, t in (("k_src", k_src), ("v_src", v_src)):
+        if t.dim() != 4 or t.shape[0] != cache.batch or t.shape[1] != cache.num_kv_heads or t.shape[3] != HEAD_DIM:
+            raise ValueError(f"{name} must be [batch, kv_heads, tokens, 128]")
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.stride(3) != 1:
+            raise ValueError(f"{name} must be a bf16 GPU tensor with unit channel stride")
+    if k_src.stride() != v_src.stride():
+        raise ValueError("k_src and v_src must have the same strides")
+    if k_src.shape[2] < max_groups * GROUP:
+        raise ValueError("source has fewer than max_groups * 128 tokens")
+    d = cache.desc()
+    sb, sh, st, _ = k_src.stride()
+    _check(lib().oscar_quantize_kv(ctypes.byref(d), k_src.data_ptr(), v_src.data_ptr(), sb, sh, st,
+                                   _ptr(dst_group_start, torch.int32, "dst_group_start"),
+                                   _ptr(num_groups, torch.int32, "num_groups"), int(max_groups),
+                                   _stream(stream)))
+
+
+def decode_workspace_bytes(batch: int, num_kv_heads: int, num_q_heads: int, max_tokens: int) -> int:
+    return int(lib().oscar_decode_workspace_bytes(batch, num_kv_heads, num_q_heads, max_tokens))
+
+
+def alloc_workspace(batch: int, num_kv_heads: int, num_q_heads: int, max_tokens: int,
+                    device="cuda") -> torch.Tensor:
+    """A zero-filled workspace (uint8) of the size the library asks for."""
+    n = decode_workspace_bytes(batch, num_kv_heads, num_q_heads, max_tokens)
+    if n == 0:
+        raise ValueError("invalid decode shape")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def workspace_init(ws: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> None:
+    _check(lib().oscar_workspace_init(_ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+
+
+def decode_attn(cache: PackedCache, n_quant: torch.Tensor, n_tail: torch.Tensor, max_tokens: int,
+                q: torch.Tensor, sm_scale: float, out: torch.Tensor, ws: torch.Tensor,
+                stream: Optional[torch.cuda.Stream] = None) -> None:
+    """oscar_decode_attn.  q bf16 [B, Hq, 128]; out fp32 [B, Hq, 128]."""
+    if q.dim() != 3 or q.shape[0] != cache.batch or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [batch, q_heads, 128]")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    d = cache.desc()
+    _check(lib().oscar_decode_attn(ctypes.byref(d), _ptr(n_quant, torch.int32, "n_quant"),
+                                   _ptr(n_tail, torch.int32, "n_tail"), int(max_tokens),
+                                   _ptr(q, torch.bfloat16, "q"), q.shape[1], float(sm_scale),
+                                   _ptr(out, torch.float32, "out"), _ptr(ws, torch.uint8, "ws"),
+                                   ws.numel(), _stream(stream)))
+
+
+def decode_attn_bf16(k: torch.Tensor, v: torch.Tensor, seq_len: torch.Tensor, max_tokens: int,
+                     q: torch.Tensor, sm_scale: float, out: torch.Tensor, ws: torch.Tensor,
+                     stream: Optional[torch.cuda.Stream] = None) -> None:
+    """oscar_decode_attn_bf16.  k, v bf16 [B, Hkv, capacity, 128]."""
+    if k.dim() != 4 or k.shape != v.shape or k.shape[3] != HEAD_DIM:
+        raise ValueError("k and v must be [batch, kv_heads, capacity, 128]")
+    if q.dim() != 3 or q.shape[0] != k.shape[0] or out.shape != q.shape:
+        raise ValueError("q / out must be [batch, q_heads, 128]")
+    B, H, C, _ = k.shape
+    _check(lib().oscar_decode_attn_bf16(_ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"), B, H, C,
+                                        _ptr(seq_len, torch.int32, "seq_len"), int(max_tokens),
+                                        _ptr(q, torch.bfloat16, "q"), q.shape[1], float(sm_scale),
+                                        _ptr(out, torch.float32, "out"), _ptr(ws, torch.uint8, "ws"),
+                                        ws.numel(), _stream(stream)))

@@ -1,0 +1,293 @@
+// Host side of the C ABI declared in include/oscar.h: argument validation,
+// split planning, workspace layout, launches and error reporting.
+#include <mutex>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "internal.hpp"
+
+namespace oscar {
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+oscar_status fail(oscar_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+oscar_status fail(oscar_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+oscar_status ok() {
+  g_last_error[0] = '\0';
+  return OSCAR_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int device_count() {
+  static std::once_flag once;
+  static int count = 0;
+  std::call_once(once, [] {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess) n = 0;
+    count = n;
+  });
+  return count;
+}
+
+oscar_status check_device(const char* fn) {
+  if (device_count() <= 0) return fail(OSCAR_EHIP, "%s: no HIP device available", fn);
+  return OSCAR_OK;
+}
+
+oscar_status launched(hipError_t e, const char* fn) {
+  if (e != hipSuccess) return fail(OSCAR_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr int64_t kTargetBlocks = 2048;
+constexpr int64_t kMinBlocks = 512;
+
+SplitPlan make_plan(int32_t batch, int32_t num_kv_heads, int32_t max_tokens) {
+  const int64_t heads = static_cast<int64_t>(batch) * num_kv_heads;
+  const int64_t T = max_tokens > 0 ? max_tokens : 0;
+  auto nsplit = [&](int64_t tps) { return (T + tps - 1) / tps; };
+  int64_t tps = 512;
+  while (heads * nsplit(tps) > kTargetBlocks && tps < (int64_t{1} << 24)) tps *= 2;
+  while (tps > OSCAR_GROUP && heads * nsplit(tps) < kMinBlocks && nsplit(tps / 2) > nsplit(tps)) tps /= 2;
+  SplitPlan p;
+  p.tokens_per_split = static_cast<int32_t>(tps);
+  p.splits = static_cast<int32_t>(nsplit(tps) > 0 ? nsplit(tps) : 1);
+  return p;
+}
+
+}  // namespace
+
+SplitPlan plan_int2(int32_t batch, int32_t num_kv_heads, int32_t max_tokens) {
+  return make_plan(batch, num_kv_heads, max_tokens);
+}
+SplitPlan plan_bf16(int32_t batch, int32_t num_kv_heads, int32_t max_tokens) {
+  return make_plan(batch, num_kv_heads, max_tokens);
+}
+
+size_t partial_bytes(int32_t batch, int32_t num_q_heads, int32_t splits) {
+  return static_cast<size_t>(batch) * num_q_heads * splits * kPartialFloats * sizeof(float);
+}
+size_t counter_offset(int32_t batch, int32_t num_q_heads, int32_t splits) {
+  return (partial_bytes(batch, num_q_heads, splits) + 255) & ~static_cast<size_t>(255);
+}
+
+namespace {
+
+__global__ void fill_zero_u32_kernel(uint32_t* p, size_t n) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+oscar_status check_heads(const char* fn, int32_t batch, int32_t num_kv_heads, int32_t num_q_heads) {
+  if (batch <= 0 || num_kv_heads <= 0 || num_q_heads <= 0)
+    return fail(OSCAR_EINVAL, "%s: batch, num_kv_heads and num_q_heads must be positive", fn);
+  if (batch > 65535 || num_kv_heads > 65535)
+    return fail(OSCAR_EINVAL, "%s: batch and num_kv_heads must be <= 65535", fn);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(OSCAR_EUNSUPPORTED, "%s: num_q_heads (%d) is not a multiple of num_kv_heads (%d)", fn,
+                num_q_heads, num_kv_heads);
+  const int g = num_q_heads / num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(OSCAR_EUNSUPPORTED, "%s: query heads per KV head must be 1, 2, 4 or 8 (got %d)", fn, g);
+  return OSCAR_OK;
+}
+
+oscar_status check_cache(const char* fn, const oscar_kv_cache* c) {
+  if (!c) return fail(OSCAR_EINVAL, "%s: cache descriptor is NULL", fn);
+  if (c->head_dim != OSCAR_HEAD_DIM) return fail(OSCAR_EUNSUPPORTED, "%s: head_dim must be 128 (got %d)", fn, c->head_dim);
+  if (c->group != OSCAR_GROUP) return fail(OSCAR_EUNSUPPORTED, "%s: group must be 128 (got %d)", fn, c->group);
+  if (c->batch <= 0 || c->num_kv_heads <= 0) return fail(OSCAR_EINVAL, "%s: batch and num_kv_heads must be positive", fn);
+  if (c->batch > 65535 || c->num_kv_heads > 65535) return fail(OSCAR_EINVAL, "%s: batch and num_kv_heads must be <= 65535", fn);
+  if (c->capacity <= 0 || c->capacity % OSCAR_GROUP != 0)
+    return fail(OSCAR_EINVAL, "%s: capacity must be a positive multiple of 128 (got %d)", fn, c->capacity);
+  const void* ptrs[5] = {c->k_codes, c->k_sz, c->k_norm, c->v_codes, c->v_sz};
+  const char* names[5] = {"k_codes", "k_sz", "k_norm", "v_codes", "v_sz"};
+  for (int i = 0; i < 5; ++i) {
+    if (!ptrs[i]) return fail(OSCAR_EINVAL, "%s: cache->%s is NULL", fn, names[i]);
+    if (!aligned16(ptrs[i])) return fail(OSCAR_EINVAL, "%s: cache->%s is not 16-byte aligned", fn, names[i]);
+  }
+  if ((c->k_tail && !aligned16(c->k_tail)) || (c->v_tail && !aligned16(c->v_tail)))
+    return fail(OSCAR_EINVAL, "%s: tail buffers must be 16-byte aligned", fn);
+  return OSCAR_OK;
+}
+
+}  // namespace
+}  // namespace oscar
+
+using namespace oscar;
+
+extern "C" {
+
+int32_t oscar_abi_version(void) { return OSCAR_ABI_VERSION; }
+
+const char* oscar_status_string(oscar_status status) {
+  switch (status) {
+    case OSCAR_OK: return "ok";
+    case OSCAR_EINVAL: return "invalid argument";
+    case OSCAR_EUNSUPPORTED: return "unsupported shape";
+    case OSCAR_EWORKSPACE: return "workspace too small";
+    case OSCAR_EHIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* oscar_last_error(void) { return g_last_error; }
+
+oscar_status oscar_quantize_kv(const oscar_kv_cache* cache, const uint16_t* k_src, const uint16_t* v_src,
+                               int64_t src_stride_b, int64_t src_stride_h, int64_t src_stride_t,
+                               const int32_t* dst_group_start, const int32_t* num_groups, int32_t max_groups,
+                               void* stream) {
+  const char* fn = "oscar_quantize_kv";
+  oscar_status st = check_cache(fn, cache);
+  if (st != OSCAR_OK) return st;
+  if (!k_src || !v_src || !dst_group_start || !num_groups)
+    return fail(OSCAR_EINVAL, "%s: source or group arrays are NULL", fn);
+  if (!aligned16(k_src) || !aligned16(v_src)) return fail(OSCAR_EINVAL, "%s: sources must be 16-byte aligned", fn);
+  if (src_stride_b < 0 || src_stride_h < 0 || src_stride_t < OSCAR_HEAD_DIM)
+    return fail(OSCAR_EINVAL, "%s: strides must be non-negative and the token stride >= 128", fn);
+  if (src_stride_b % 8 || src_stride_h % 8 || src_stride_t % 8)
+    return fail(OSCAR_EINVAL, "%s: strides must be multiples of 8 elements (16 bytes)", fn);
+  if (max_groups < 0) return fail(OSCAR_EINVAL, "%s: max_groups must be >= 0", fn);
+  if (max_groups > cache->capacity / OSCAR_GROUP)
+    return fail(OSCAR_EINVAL, "%s: max_groups (%d) exceeds the cache's %d groups", fn, max_groups,
+                cache->capacity / OSCAR_GROUP);
+  if (max_groups == 0) return ok();
+  if ((st = check_device(fn)) != OSCAR_OK) return st;
+  QuantizeArgs a;
+  a.k_codes = cache->k_codes;
+  a.k_sz = cache->k_sz;
+  a.k_norm = cache->k_norm;
+  a.v_codes = cache->v_codes;
+  a.v_sz = cache->v_sz;
+  a.k_src = k_src;
+  a.v_src = v_src;
+  a.sb = src_stride_b;
+  a.sh = src_stride_h;
+  a.st = src_stride_t;
+  a.dst_group_start = dst_group_start;
+  a.num_groups = num_groups;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.capacity = cache->capacity;
+  return launched(launch_quantize(a, cache->batch, max_groups, static_cast<hipStream_t>(stream)), fn);
+}
+
+size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t num_q_heads, int32_t max_tokens) {
+  if (batch <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 || max_tokens < 0) return 0;
+  if (num_q_heads % num_kv_heads != 0) return 0;
+  const SplitPlan pi = plan_int2(batch, num_kv_heads, max_tokens);
+  const SplitPlan pb = plan_bf16(batch, num_kv_heads, max_tokens);
+  const int32_t splits = pi.splits > pb.splits ? pi.splits : pb.splits;
+  return counter_offset(batch, num_q_heads, splits) + static_cast<size_t>(batch) * num_kv_heads * sizeof(uint32_t);
+}
+
+oscar_status oscar_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "oscar_workspace_init";
+  if (!ws) return fail(OSCAR_EINVAL, "%s: workspace is NULL", fn);
+  if (!aligned16(ws)) return fail(OSCAR_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+  const size_t n = ws_bytes / sizeof(uint32_t);
+  if (n == 0) return ok();
+  oscar_status st = check_device(fn);
+  if (st != OSCAR_OK) return st;
+  return launched(launch_fill_zero_u32(static_cast<uint32_t*>(ws), n, static_cast<hipStream_t>(stream)), fn);
+}
+
+oscar_status oscar_decode_attn(const oscar_kv_cache* cache, const int32_t* n_quant, const int32_t* n_tail,
+                               int32_t max_tokens, const uint16_t* q, int32_t num_q_heads, float sm_scale,
+                               float* out, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "oscar_decode_attn";
+  oscar_status st = check_cache(fn, cache);
+  if (st != OSCAR_OK) return st;
+  if ((st = check_heads(fn, cache->batch, cache->num_kv_heads, num_q_heads)) != OSCAR_OK) return st;
+  if (!n_quant || !n_tail || !q || !out || !ws) return fail(OSCAR_EINVAL, "%s: NULL argument", fn);
+  if (!aligned16(q) || !aligned16(out) || !aligned16(ws))
+    return fail(OSCAR_EINVAL, "%s: q, out and ws must be 16-byte aligned", fn);
+  if (max_tokens < 0) return fail(OSCAR_EINVAL, "%s: max_tokens must be >= 0", fn);
+  if (max_tokens > cache->capacity + OSCAR_GROUP - 1)
+    return fail(OSCAR_EINVAL, "%s: max_tokens (%d) exceeds capacity + 127", fn, max_tokens);
+  const size_t need = oscar_decode_workspace_bytes(cache->batch, cache->num_kv_heads, num_q_heads, max_tokens);
+  if (ws_bytes < need) return fail(OSCAR_EWORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, ws_bytes, need);
+  if ((st = check_device(fn)) != OSCAR_OK) return st;
+  const SplitPlan p = plan_int2(cache->batch, cache->num_kv_heads, max_tokens);
+  DecodeInt2Args a;
+  a.k_codes = cache->k_codes;
+  a.k_sz = cache->k_sz;
+  a.k_norm = cache->k_norm;
+  a.v_codes = cache->v_codes;
+  a.v_sz = cache->v_sz;
+  a.k_tail = cache->k_tail;
+  a.v_tail = cache->v_tail;
+  a.n_quant = n_quant;
+  a.n_tail = n_tail;
+  a.q = q;
+  a.out = out;
+  a.partials = static_cast<float*>(ws);
+  const SplitPlan pb = plan_bf16(cache->batch, cache->num_kv_heads, max_tokens);
+  const int32_t ws_splits = p.splits > pb.splits ? p.splits : pb.splits;
+  a.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + counter_offset(cache->batch, num_q_heads, ws_splits));
+  a.num_kv_heads = cache->num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.capacity = cache->capacity;
+  a.max_tokens = max_tokens;
+  a.tokens_per_split = p.tokens_per_split;
+  a.splits = p.splits;
+  a.sm_scale = sm_scale;
+  return launched(launch_decode_int2(a, cache->batch, static_cast<hipStream_t>(stream)), fn);
+}
+
+oscar_status oscar_decode_attn_bf16(const uint16_t* k, const uint16_t* v, int32_t batch, int32_t num_kv_heads,
+                                    int32_t capacity, const int32_t* seq_len, int32_t max_tokens, const uint16_t* q,
+                                    int32_t num_q_heads, float sm_scale, float* out, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  const char* fn = "oscar_decode_attn_bf16";
+  oscar_status st = check_heads(fn, batch, num_kv_heads, num_q_heads);
+  if (st != OSCAR_OK) return st;
+  if (!k || !v || !seq_len || !q || !out || !ws) return fail(OSCAR_EINVAL, "%s: NULL argument", fn);
+  if (!aligned16(k) || !aligned16(v) || !aligned16(q) || !aligned16(out) || !aligned16(ws))
+    return fail(OSCAR_EINVAL, "%s: k, v, q, out and ws must be 16-byte aligned", fn);
+  if (capacity <= 0) return fail(OSCAR_EINVAL, "%s: capacity must be positive", fn);
+  if (max_tokens < 0 || max_tokens > capacity)
+    return fail(OSCAR_EINVAL, "%s: max_tokens must be in [0, capacity]", fn);
+  const size_t need = oscar_decode_workspace_bytes(batch, num_kv_heads, num_q_heads, max_tokens);
+  if (ws_bytes < need) return fail(OSCAR_EWORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, ws_bytes, need);
+  if ((st = check_device(fn)) != OSCAR_OK) return st;
+  const SplitPlan p = plan_bf16(batch, num_kv_heads, max_tokens);
+  const SplitPlan pi = plan_int2(batch, num_kv_heads, max_tokens);
+  const int32_t ws_splits = p.splits > pi.splits ? p.splits : pi.splits;
+  DecodeBf16Args a;
+  a.k = k;
+  a.v = v;
+  a.seq_len = seq_len;
+  a.q = q;
+  a.out = out;
+  a.partials = static_cast<float*>(ws);
+  a.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + counter_offset(batch, num_q_heads, ws_splits));
+  a.num_kv_heads = num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.capacity = capacity;
+  a.max_tokens = max_tokens;
+  a.tokens_per_split = p.tokens_per_split;
+  a.splits = p.splits;
+  a.sm_scale = sm_scale;
+  return launched(launch_decode_bf16(a, batch, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"
+
+namespace oscar {
+hipError_t launch_fill_zero_u32(uint32_t* p, size_t n, hipStream_t s) {
+  const unsigned threads = 256;
+  const size_t blocks = (n + threads - 1) / threads;
+  hipLaunchKernelGGL(fill_zero_u32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, s, p, n);
+  return hipGetLastError();
+}
+}  // namespace oscar

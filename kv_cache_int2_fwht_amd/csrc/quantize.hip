@@ -1,0 +1,230 @@
+// OScaR quantizer kernel: Canalized Rotation + Omni-Token Scaling +
+// per-channel INT2 for keys, per-token INT2 for values, 2-bit packing.
+//
+// Method: OScaR abstract (arXiv 2605.19660, fugumt.com record, "Abstract");
+// ai-papers.net OScaR summary, section "OScaRの提案手法" and Fig. 4 (rotation
+// first, then per-token L2 scaling).  The INT2 formula (asymmetric min/max,
+// fp16 scale and zero-point, round half to even) and the packed layout are
+// this library's readings of what the pages leave open.
+//
+// One workgroup (4 waves) quantizes one 128-token group of one (sequence,
+// KV head).  Every quantity that decides an fp16 parameter or a code is
+// computed in fp64: the Hadamard butterflies on bf16 inputs are then exact
+// in practice, so the stored norms, scales, zero-points and codes are the
+// ones an fp64 evaluation of the same formulas gives.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace oscar {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr double kSqrt128 = 0x1.6a09e667f3bcdp+3;  // 8 * sqrt(2)
+
+__device__ __forceinline__ uint32_t code_from(double x, double z, double inv_s) {
+  // inv_s == 0 encodes s == 0: r = 0 and the code is 0.
+  const double r = (x - z) * inv_s;
+  const double c = fmin(fmax(rint(r), 0.0), 3.0);
+  return static_cast<uint32_t>(c);
+}
+
+__global__ __launch_bounds__(kThreads) void quantize_kv_kernel(QuantizeArgs a) {
+  const int j = blockIdx.x;   // source group
+  const int h = blockIdx.y;   // KV head
+  const int b = blockIdx.z;   // sequence
+  if (j >= a.num_groups[b]) return;
+  const int groups_cap = a.capacity / kGroup;
+  const int dst = a.dst_group_start[b] + j;
+  if (dst < 0 || dst >= groups_cap) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const size_t slice = static_cast<size_t>(b) * a.num_kv_heads + h;
+  const size_t tok0 = slice * a.capacity + static_cast<size_t>(dst) * kGroup;
+  const size_t grp = slice * groups_cap + dst;
+  const uint16_t* ksrc = a.k_src + b * a.sb + h * a.sh + static_cast<int64_t>(j) * kGroup * a.st;
+  const uint16_t* vsrc = a.v_src + b * a.sb + h * a.sh + static_cast<int64_t>(j) * kGroup * a.st;
+
+  __shared__ double red_min[16][kHeadDim];
+  __shared__ double red_max[16][kHeadDim];
+  __shared__ double zs[kHeadDim];
+  __shared__ double inv_s[kHeadDim];
+  __shared__ double vz[kGroup];
+  __shared__ double vinv[kGroup];
+
+  // ---------------- keys ----------------
+  // Lane = (slot, L): 4 lanes per token, lane L holds channels 32L..32L+31.
+  // A wave covers 16 tokens per pass, two passes: tokens wave*32 + pass*16 + slot.
+  const int L = lane & 3;
+  const int slot = lane >> 2;
+  double u[2][32];
+  uint16_t n16_bits[2];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int t = wave * 32 + pass * 16 + slot;
+    const uint4* src = reinterpret_cast<const uint4*>(ksrc + static_cast<int64_t>(t) * a.st + 32 * L);
+    double* x = u[pass];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 w = src[q];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * q + 2 * e] = static_cast<double>(bf16lo_to_f32(ws[e]));
+        x[8 * q + 2 * e + 1] = static_cast<double>(bf16hi_to_f32(ws[e]));
+      }
+    }
+    // Unnormalised Walsh-Hadamard butterflies, channel bits 0..4 in-lane.
+#pragma unroll
+    for (int bit = 1; bit < 32; bit <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (!(i & bit)) {
+          const double p = x[i], r = x[i | bit];
+          x[i] = p + r;
+          x[i | bit] = p - r;
+        }
+      }
+    }
+    // Channel bit 5 = lane bit 0, channel bit 6 = lane bit 1 (DPP within the quad).
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const double p = dpp_f64<kDppQuadXor1>(x[i]);
+      x[i] = (L & 1) ? (p - x[i]) : (x[i] + p);
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const double p = dpp_f64<kDppQuadXor2>(x[i]);
+      x[i] = (L & 2) ? (p - x[i]) : (x[i] + p);
+    }
+    // ||y||^2 = sum(Y^2) / 128 for the unnormalised transform Y = sqrt(128) y.
+    double ssq = 0.0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) ssq = fma(x[i], x[i], ssq);
+    ssq += dpp_f64<kDppQuadXor1>(ssq);   // a + b == b + a: all four lanes agree
+    ssq += dpp_f64<kDppQuadXor2>(ssq);
+    const double n = sqrt(ssq * (1.0 / 128.0));
+    n16_bits[pass] = f64_to_f16_bits_rne_sat(n);
+    const double n16 = f16_bits_to_f64(n16_bits[pass]);
+    const double inv = (n16 > 0.0) ? 1.0 / (n16 * kSqrt128) : 0.0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] *= inv;
+  }
+  // Per-channel min / max over this lane's two tokens, then over the four
+  // token slots of each 16-lane row.
+  double mn[32], mx[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    mn[i] = fmin(u[0][i], u[1][i]);
+    mx[i] = fmax(u[0][i], u[1][i]);
+    mn[i] = fmin(mn[i], dpp_f64<kDppRowRor4>(mn[i]));
+    mx[i] = fmax(mx[i], dpp_f64<kDppRowRor4>(mx[i]));
+    mn[i] = fmin(mn[i], dpp_f64<kDppRowRor8>(mn[i]));
+    mx[i] = fmax(mx[i], dpp_f64<kDppRowRor8>(mx[i]));
+  }
+  const int row = wave * 4 + (lane >> 4);
+  if ((lane & 15) < 4) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      red_min[row][32 * L + i] = mn[i];
+      red_max[row][32 * L + i] = mx[i];
+    }
+  }
+  __syncthreads();
+  if (tid < kHeadDim) {
+    double lo = red_min[0][tid], hi = red_max[0][tid];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      lo = fmin(lo, red_min[r][tid]);
+      hi = fmax(hi, red_max[r][tid]);
+    }
+    const uint16_t s_bits = f64_to_f16_bits_rne_sat((hi - lo) / 3.0);
+    const uint16_t z_bits = f64_to_f16_bits_rne_sat(lo);
+    reinterpret_cast<uint32_t*>(a.k_sz)[grp * kHeadDim + tid] =
+        static_cast<uint32_t>(s_bits) | (static_cast<uint32_t>(z_bits) << 16);
+    const double s16 = f16_bits_to_f64(s_bits);
+    zs[tid] = f16_bits_to_f64(z_bits);
+    inv_s[tid] = (s16 > 0.0) ? 1.0 / s16 : 0.0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int t = wave * 32 + pass * 16 + slot;
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      w0 |= code_from(u[pass][i], zs[32 * L + i], inv_s[32 * L + i]) << (2 * i);
+      w1 |= code_from(u[pass][16 + i], zs[32 * L + 16 + i], inv_s[32 * L + 16 + i]) << (2 * i);
+    }
+    *reinterpret_cast<uint2*>(a.k_codes + (tok0 + t) * 32 + 8 * L) = make_uint2(w0, w1);
+    if (L == 0) a.k_norm[tok0 + t] = n16_bits[pass];
+  }
+
+  // ---------------- values ----------------
+  // Statistics: 16 lanes per token, 8 channels per lane, 4 tokens per wave pass.
+  {
+    const int cb = lane & 15;
+    const int tslot = lane >> 4;
+#pragma unroll 2
+    for (int pass = 0; pass < 8; ++pass) {
+      const int t = wave * 32 + pass * 4 + tslot;
+      const uint4 w = *reinterpret_cast<const uint4*>(vsrc + static_cast<int64_t>(t) * a.st + 8 * cb);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      float lo = bf16lo_to_f32(ws[0]), hi = lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f0 = bf16lo_to_f32(ws[e]), f1 = bf16hi_to_f32(ws[e]);
+        lo = fminf(lo, fminf(f0, f1));
+        hi = fmaxf(hi, fmaxf(f0, f1));
+      }
+      lo = fminf(lo, dpp_f32<kDppQuadXor1>(lo));
+      hi = fmaxf(hi, dpp_f32<kDppQuadXor1>(hi));
+      lo = fminf(lo, dpp_f32<kDppQuadXor2>(lo));
+      hi = fmaxf(hi, dpp_f32<kDppQuadXor2>(hi));
+      lo = fminf(lo, dpp_f32<kDppRowRor4>(lo));
+      hi = fmaxf(hi, dpp_f32<kDppRowRor4>(hi));
+      lo = fminf(lo, dpp_f32<kDppRowRor8>(lo));
+      hi = fmaxf(hi, dpp_f32<kDppRowRor8>(hi));
+      if (cb == 0) {
+        const uint16_t s_bits = f64_to_f16_bits_rne_sat((static_cast<double>(hi) - static_cast<double>(lo)) / 3.0);
+        const uint16_t z_bits = f64_to_f16_bits_rne_sat(static_cast<double>(lo));
+        reinterpret_cast<uint32_t*>(a.v_sz)[tok0 + t] =
+            static_cast<uint32_t>(s_bits) | (static_cast<uint32_t>(z_bits) << 16);
+        const double s16 = f16_bits_to_f64(s_bits);
+        vz[t] = f16_bits_to_f64(z_bits);
+        vinv[t] = (s16 > 0.0) ? 1.0 / s16 : 0.0;
+      }
+    }
+  }
+  __syncthreads();
+  // Codes: thread = (channel d, half of the group's tokens); one 16-byte store.
+  {
+    const int d = tid & (kHeadDim - 1);
+    const int half = tid >> 7;
+    uint32_t words[4];
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int t = half * 64 + wd * 16 + e;
+        const double v = static_cast<double>(bf16_to_f32(vsrc[static_cast<int64_t>(t) * a.st + d]));
+        acc |= code_from(v, vz[t], vinv[t]) << (2 * e);
+      }
+      words[wd] = acc;
+    }
+    *reinterpret_cast<uint4*>(a.v_codes + (grp * kHeadDim + d) * 32 + 16 * half) =
+        make_uint4(words[0], words[1], words[2], words[3]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantizeArgs& a, int32_t batch, int32_t max_groups, hipStream_t s) {
+  dim3 grid(max_groups, a.num_kv_heads, batch);
+  hipLaunchKernelGGL(quantize_kv_kernel, grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace oscar

@@ -1,0 +1,134 @@
+"""The C ABI library on the host: it loads, exports every function that
+include/oscar.h declares, and validates arguments before touching a device.
+
+Tests that pass placeholder pointers run only where no GPU is present: there
+the library must stop at validation (or report that no device exists)
+without launching anything.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_int2_fwht_amd import binding as ob
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oscar.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    names = set(re.findall(r"\b(oscar_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function():
+    L = ob.lib()
+    declared = _declared_functions()
+    assert len(declared) >= 8
+    for name in declared:
+        assert hasattr(L, name), f"{name} declared in oscar.h but not exported"
+    assert set(declared) == set(ob.EXPORTED)
+
+
+def test_version_and_status_strings():
+    assert ob.abi_version() == 1
+    assert ob.status_string(0) == "ok"
+    assert ob.status_string(3) == "workspace too small"
+    assert ob.status_string(99) == "unknown status"
+
+
+def test_workspace_size_rules():
+    f = ob.decode_workspace_bytes
+    assert f(0, 8, 32, 1024) == 0
+    assert f(1, 8, 30, 1024) == 0          # 30 query heads over 8 KV heads
+    assert f(1, 8, 32, -1) == 0
+    small, big = f(1, 8, 32, 8192), f(1, 8, 32, 131072)
+    assert 0 < small <= big
+    assert f(1, 8, 32, 0) > 0              # an empty cache still needs the counters
+    # counters sit at the end, 4 bytes per (sequence, KV head)
+    assert f(8, 8, 32, 131072) >= 8 * 8 * 4
+
+
+def _no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+needs_no_gpu = pytest.mark.skipif(not _no_gpu(), reason="placeholder pointers are only passed where no GPU exists")
+
+
+def _desc(**kw):
+    d = dict(batch=1, num_kv_heads=8, head_dim=128, group=128, capacity=1024,
+             k_codes=0x10000, k_sz=0x20000, k_norm=0x30000, v_codes=0x40000, v_sz=0x50000,
+             k_tail=0x60000, v_tail=0x70000)
+    d.update(kw)
+    return ob.KVCacheDesc(*[d[f] for f, _ in ob.KVCacheDesc._fields_])
+
+
+def _decode(desc, hq=32, max_tokens=1024, ws_bytes=1 << 26, q=0x80000, out=0x90000, ws=0xA0000):
+    L = ob.lib()
+    return L.oscar_decode_attn(ctypes.byref(desc) if desc is not None else None, 0x100, 0x200, max_tokens, q, hq,
+                               0.088, out, ws, ws_bytes, None)
+
+
+@needs_no_gpu
+def test_decode_validation_errors():
+    L = ob.lib()
+    assert _decode(None) == ob.OSCAR_EINVAL
+    assert b"NULL" in L.oscar_last_error()
+    assert _decode(_desc(head_dim=64)) == ob.OSCAR_EUNSUPPORTED
+    assert _decode(_desc(group=64)) == ob.OSCAR_EUNSUPPORTED
+    assert _decode(_desc(capacity=1000)) == ob.OSCAR_EINVAL
+    assert _decode(_desc(k_codes=0)) == ob.OSCAR_EINVAL
+    assert _decode(_desc(v_sz=0x50008)) == ob.OSCAR_EINVAL          # misaligned
+    assert _decode(_desc(), hq=30) == ob.OSCAR_EUNSUPPORTED           # not a multiple of 8 KV heads
+    assert _decode(_desc(), hq=24) == ob.OSCAR_EUNSUPPORTED           # 3 query heads per KV head
+    assert _decode(_desc(), max_tokens=-1) == ob.OSCAR_EINVAL
+    assert _decode(_desc(), max_tokens=1024 + 128) == ob.OSCAR_EINVAL  # beyond capacity + 127
+    assert _decode(_desc(), ws_bytes=64) == ob.OSCAR_EWORKSPACE
+    assert b"workspace" in L.oscar_last_error()
+    assert _decode(_desc(), q=0x80004) == ob.OSCAR_EINVAL
+
+
+@needs_no_gpu
+def test_valid_call_without_device_reports_hip_error():
+    assert _decode(_desc()) == ob.OSCAR_EHIP
+    assert b"no HIP device" in ob.lib().oscar_last_error()
+
+
+@needs_no_gpu
+def test_quantize_validation_errors():
+    L = ob.lib()
+
+    def q(desc, k=0xB0000, v=0xC0000, sb=8 * 1024 * 128, sh=1024 * 128, st=128, starts=0x100, ng=0x200, mg=8):
+        return L.oscar_quantize_kv(ctypes.byref(desc), k, v, sb, sh, st, starts, ng, mg, None)
+
+    assert q(_desc(), k=0) == ob.OSCAR_EINVAL
+    assert q(_desc(), k=0xB0002) == ob.OSCAR_EINVAL
+    assert q(_desc(), st=64) == ob.OSCAR_EINVAL
+    assert q(_desc(), st=132) == ob.OSCAR_EINVAL          # not a multiple of 8 elements
+    assert q(_desc(), mg=-1) == ob.OSCAR_EINVAL
+    assert q(_desc(), mg=9) == ob.OSCAR_EINVAL            # more groups than the cache holds
+    assert q(_desc(), mg=0) == ob.OSCAR_OK                # nothing to do
+    assert q(_desc(head_dim=256)) == ob.OSCAR_EUNSUPPORTED
+    assert q(_desc()) == ob.OSCAR_EHIP                    # valid, but no device here
+
+
+@needs_no_gpu
+def test_bf16_validation_errors():
+    L = ob.lib()
+
+    def d(k=0x10000, v=0x20000, B=1, H=8, C=1024, hq=32, mt=1024, ws_bytes=1 << 26):
+        return L.oscar_decode_attn_bf16(k, v, B, H, C, 0x100, mt, 0x30000, hq, 0.088, 0x40000, 0x50000,
+                                        ws_bytes, None)
+
+    assert d(k=0) == ob.OSCAR_EINVAL
+    assert d(B=0) == ob.OSCAR_EINVAL
+    assert d(hq=12) == ob.OSCAR_EUNSUPPORTED
+    assert d(mt=2048) == ob.OSCAR_EINVAL
+    assert d(ws_bytes=10) == ob.OSCAR_EWORKSPACE
+    assert d() == ob.OSCAR_EHIP

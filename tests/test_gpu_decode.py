@@ -1,0 +1,154 @@
+"""GPU parity of oscar_decode_attn (on the oracle's packed bytes) and of
+oscar_decode_attn_bf16 against the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as syn
+from tests.helpers import assert_out_close, bits_to_dev_bf16, upload_slice
+
+pytestmark = pytest.mark.gpu
+
+SM = 1.0 / np.sqrt(128.0)
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _build(ob, w, dev, capacity=None):
+    """Oracle slices of every (b, h), uploaded into a PackedCache, plus the
+    raw bf16 K/V (for the bf16 kernel) and the queries."""
+    B, H, Hq = w.batch, w.num_kv_heads, w.num_q_heads
+    lens = [w.total_tokens(b) for b in range(B)]
+    nq = [syn.split_lengths(n)[0] for n in lens]
+    cap = capacity or max(128, max(((n + 127) // 128) * 128 for n in lens))
+    cache = ob.PackedCache(B, H, cap, device=dev)
+    kraw = np.zeros((B, H, cap, 128), np.uint16)
+    vraw = np.zeros((B, H, cap, 128), np.uint16)
+    slices = {}
+    for b in range(B):
+        for h in range(H):
+            kb, vb = syn.keys_slice(w, b, h), syn.values_slice(w, b, h)
+            kraw[b, h, :lens[b]] = kb
+            vraw[b, h, :lens[b]] = vb
+            s = oracle.quantize_slice(syn.bf16_bits_to_f64(kb), syn.bf16_bits_to_f64(vb), nq[b])
+            upload_slice(cache, b, h, s)
+            slices[b, h] = s
+    q = np.stack([syn.query(w, b) for b in range(B)])
+    return cache, slices, kraw, vraw, q, lens, nq
+
+
+def _oracle_out(w, slices, q, lens):
+    G = w.num_q_heads // w.num_kv_heads
+    out = np.zeros((w.batch, w.num_q_heads, 128))
+    for b in range(w.batch):
+        for h in range(w.num_kv_heads):
+            qq = syn.bf16_bits_to_f64(q[b, h * G:(h + 1) * G])
+            out[b, h * G:(h + 1) * G] = slices[b, h].decode(qq, SM)
+    return out
+
+
+def _run_int2(ob, cache, q, lens, nq, dev, max_tokens=None):
+    B, Hq = q.shape[0], q.shape[1]
+    mt = max(lens) if max_tokens is None else max_tokens
+    qd = bits_to_dev_bf16(q, dev)
+    out = torch.full((B, Hq, 128), float("nan"), dtype=torch.float32, device=dev)
+    ws = ob.alloc_workspace(B, cache.num_kv_heads, Hq, mt, device=dev)
+    ob.decode_attn(cache, torch.tensor(nq, dtype=torch.int32, device=dev),
+                   torch.tensor([n - m for n, m in zip(lens, nq)], dtype=torch.int32, device=dev),
+                   mt, qd, SM, out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), ws
+
+
+CASES = {
+    "cfg0": lambda: syn.workload(0),
+    "cfg1": lambda: syn.workload(1),
+    "ragged_g4": lambda: syn.custom_workload(4, 8, 2, [0, 77, 128, 1000 + 5], cfg_tag=102),
+    "g1_tail": lambda: syn.custom_workload(2, 3, 3, [300, 2048 + 127], cfg_tag=103),
+    "g2": lambda: syn.custom_workload(1, 4, 2, [5000], cfg_tag=104),
+    "g8": lambda: syn.custom_workload(2, 16, 2, [1, 4096 + 64], cfg_tag=105),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_int2_decode_matches_oracle(gpu_lib, case):
+    from kv_cache_int2_fwht_amd import binding as ob
+    dev = torch.device("cuda:0")
+    w = CASES[case]()
+    _say(f"int2 decode {case}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} lens={w.lengths}")
+    cache, slices, _, _, q, lens, nq = _build(ob, w, dev)
+    got, _ = _run_int2(ob, cache, q, lens, nq, dev)
+    err = assert_out_close(got, _oracle_out(w, slices, q, lens), case)
+    _say(f"  max abs err {err:.2e}")
+
+
+def test_int2_decode_grid_larger_than_lengths(gpu_lib):
+    """max_tokens far above the real lengths: extra splits see no tokens."""
+    from kv_cache_int2_fwht_amd import binding as ob
+    dev = torch.device("cuda:0")
+    w = syn.custom_workload(2, 8, 2, [700, 129], cfg_tag=106)
+    cache, slices, _, _, q, lens, nq = _build(ob, w, dev, capacity=8192)
+    got, _ = _run_int2(ob, cache, q, lens, nq, dev, max_tokens=8192)
+    assert_out_close(got, _oracle_out(w, slices, q, lens), "oversized grid")
+
+
+def test_int2_decode_empty_and_deterministic(gpu_lib):
+    from kv_cache_int2_fwht_amd import binding as ob
+    dev = torch.device("cuda:0")
+    w = syn.custom_workload(2, 4, 1, [0, 3000], cfg_tag=107)
+    cache, slices, _, _, q, lens, nq = _build(ob, w, dev)
+    a, ws = _run_int2(ob, cache, q, lens, nq, dev)
+    b, _ = _run_int2(ob, cache, q, lens, nq, dev)
+    assert np.array_equal(a, b)
+    assert np.all(a[0] == 0.0)
+    # the workspace's arrival counters are back at zero after every call
+    counters = ws[-(w.batch * w.num_kv_heads) * 4:].view(torch.int32)
+    assert int(counters.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("case", ["cfg0", "cfg1", "ragged_g4", "g8"])
+def test_bf16_decode_matches_oracle(gpu_lib, case):
+    from kv_cache_int2_fwht_amd import binding as ob
+    dev = torch.device("cuda:0")
+    w = CASES[case]()
+    _say(f"bf16 decode {case}")
+    B, H, Hq = w.batch, w.num_kv_heads, w.num_q_heads
+    lens = [w.total_tokens(b) for b in range(B)]
+    cap = max(128, max(lens))
+    k = np.zeros((B, H, cap, 128), np.uint16)
+    v = np.zeros((B, H, cap, 128), np.uint16)
+    for b in range(B):
+        for h in range(H):
+            k[b, h, :lens[b]] = syn.keys_slice(w, b, h)
+            v[b, h, :lens[b]] = syn.values_slice(w, b, h)
+    q = np.stack([syn.query(w, b) for b in range(B)])
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    ws = ob.alloc_workspace(B, H, Hq, max(lens), device=dev)
+    ob.decode_attn_bf16(bits_to_dev_bf16(k, dev), bits_to_dev_bf16(v, dev),
+                        torch.tensor(lens, dtype=torch.int32, device=dev), max(lens),
+                        bits_to_dev_bf16(q, dev), SM, out, ws)
+    torch.cuda.synchronize()
+    G = Hq // H
+    ref = np.zeros((B, Hq, 128))
+    for b in range(B):
+        for h in range(H):
+            ref[b, h * G:(h + 1) * G] = oracle.decode_bf16_slice(
+                syn.bf16_bits_to_f64(q[b, h * G:(h + 1) * G]), syn.bf16_bits_to_f64(k[b, h, :lens[b]]),
+                syn.bf16_bits_to_f64(v[b, h, :lens[b]]), SM)
+    assert_out_close(out.cpu().numpy(), ref, case)
+
+
+def test_workspace_too_small_is_an_error(gpu_lib):
+    from kv_cache_int2_fwht_amd import binding as ob
+    dev = torch.device("cuda:0")
+    cache = ob.PackedCache(1, 1, 1024, device=dev)
+    q = torch.zeros((1, 1, 128), dtype=torch.bfloat16, device=dev)
+    out = torch.zeros((1, 1, 128), dtype=torch.float32, device=dev)
+    ws = torch.zeros(16, dtype=torch.uint8, device=dev)
+    z = torch.zeros(1, dtype=torch.int32, device=dev)
+    with pytest.raises(ob.OscarError) as e:
+        ob.decode_attn(cache, z, z, 1024, q, SM, out, ws)
+    assert e.value.status == ob.OSCAR_EWORKSPACE

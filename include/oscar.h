@@ -136,21 +136,12 @@ oscar_status oscar_quantize_kv(const oscar_kv_cache* cache,
 
 /*
  * Bytes of workspace that oscar_decode_attn / oscar_decode_attn_bf16 need
- * for this shape: split-K partial softmax states (m, l, acc[128]) per query
- * head and split, plus one arrival counter per (sequence, KV head).
- * Returns 0 for invalid shapes.
+ * for this shape: the split-K partial softmax states (m, l, acc[128]) of
+ * every query head and split.  Returns 0 for invalid shapes.  The
+ * workspace needs no initialisation.
  */
 size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_kv_heads,
                                     int32_t num_q_heads, int32_t max_tokens);
-
-/*
- * Zero the arrival counters of a workspace (a fill kernel, no hipMemset).
- * A workspace must be zero when first used; every decode call leaves its
- * counters at zero again, so this is needed once per allocation (a buffer
- * from a zero-filling allocator needs no call).  Calls that share one
- * workspace must be ordered on one stream.
- */
-oscar_status oscar_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /*
  * oscar_decode_attn -- one decode step over the packed INT2 cache.
@@ -161,8 +152,9 @@ oscar_status oscar_workspace_init(void* ws, size_t ws_bytes, void* stream);
  * sm_scale * (q . k_tail), take the softmax over all n_quant[b] + n_tail[b]
  * tokens and write out = sum_t p_t * value_t (values dequantized as
  * s * c + z, tail values as stored).  The token range is split across
- * workgroups and the partial softmax states are merged in a fixed order, so
- * results are deterministic.  An empty sequence gives out = 0.
+ * workgroups; a second kernel on the same stream merges their partial
+ * softmax states in a fixed order, so results are deterministic.  An empty
+ * sequence gives out = 0.
  *
  * n_quant      : device int32[batch]; quantized tokens, a multiple of 128,
  *                <= capacity (precondition).
@@ -173,9 +165,9 @@ oscar_status oscar_workspace_init(void* ws, size_t ws_bytes, void* stream);
  * sm_scale     : logit scale (usually 1/sqrt(128)).
  * out          : fp32 [batch][num_q_heads][128].
  * ws, ws_bytes : workspace of at least oscar_decode_workspace_bytes(batch,
- *                num_kv_heads, num_q_heads, max_tokens) bytes, counters
- *                zero (see oscar_workspace_init).  Calls that share a
- *                workspace must not overlap.
+ *                num_kv_heads, num_q_heads, max_tokens) bytes.  Calls that
+ *                share a workspace must not overlap (ordering them on one
+ *                stream is enough).
  */
 oscar_status oscar_decode_attn(const oscar_kv_cache* cache,
                                const int32_t* n_quant, const int32_t* n_tail,

@@ -6,7 +6,7 @@ The compute path is the HIP library ``_lib/liboscar.so`` (C ABI in
 """
 from . import binding  # noqa: F401
 from .binding import (PackedCache, OscarError, quantize_kv, decode_attn, decode_attn_bf16,  # noqa: F401
-                      decode_workspace_bytes, alloc_workspace, workspace_init)
+                      decode_workspace_bytes, alloc_workspace)
 
 __all__ = ["binding", "PackedCache", "OscarError", "quantize_kv", "decode_attn",
-           "decode_attn_bf16", "decode_workspace_bytes", "alloc_workspace", "workspace_init"]
+           "decode_attn_bf16", "decode_workspace_bytes", "alloc_workspace"]

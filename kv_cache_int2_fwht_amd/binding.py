@@ -49,7 +49,7 @@ class KVCacheDesc(ctypes.Structure):
 
 EXPORTED = (
     "oscar_abi_version", "oscar_status_string", "oscar_last_error",
-    "oscar_quantize_kv", "oscar_decode_workspace_bytes", "oscar_workspace_init",
+    "oscar_quantize_kv", "oscar_decode_workspace_bytes",
     "oscar_decode_attn", "oscar_decode_attn_bf16",
 )
 
@@ -78,8 +78,6 @@ def lib():
     L.oscar_quantize_kv.argtypes = [ctypes.POINTER(KVCacheDesc), vp, vp, i64, i64, i64, vp, vp, i32, vp]
     L.oscar_decode_workspace_bytes.restype = sz
     L.oscar_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
-    L.oscar_workspace_init.restype = ctypes.c_int
-    L.oscar_workspace_init.argtypes = [vp, sz, vp]
     L.oscar_decode_attn.restype = ctypes.c_int
     L.oscar_decode_attn.argtypes = [ctypes.POINTER(KVCacheDesc), vp, vp, i32, vp, i32, f32, vp, vp, sz, vp]
     L.oscar_decode_attn_bf16.restype = ctypes.c_int
@@ -189,15 +187,11 @@ def decode_workspace_bytes(batch: int, num_kv_heads: int, num_q_heads: int, max_
 
 def alloc_workspace(batch: int, num_kv_heads: int, num_q_heads: int, max_tokens: int,
                     device="cuda") -> torch.Tensor:
-    """A zero-filled workspace (uint8) of the size the library asks for."""
+    """A workspace (uint8) of the size the library asks for."""
     n = decode_workspace_bytes(batch, num_kv_heads, num_q_heads, max_tokens)
     if n == 0:
         raise ValueError("invalid decode shape")
-    return torch.zeros(n, dtype=torch.uint8, device=device)
-
-
-def workspace_init(ws: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> None:
-    _check(lib().oscar_workspace_init(_ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def decode_attn(cache: PackedCache, n_quant: torch.Tensor, n_tail: torch.Tensor, max_tokens: int,

@@ -49,7 +49,9 @@ oscar_status launched(hipError_t e, const char* fn) {
   return ok();
 }
 
-constexpr int64_t kTargetBlocks = 2048;
+// About two workgroups per compute unit: each wave then streams several
+// groups back to back (prefetching the next while computing the current).
+constexpr int64_t kTargetBlocks = 512;
 constexpr int64_t kMinBlocks = 512;
 
 SplitPlan make_plan(int32_t batch, int32_t num_kv_heads, int32_t max_tokens) {
@@ -77,16 +79,8 @@ SplitPlan plan_bf16(int32_t batch, int32_t num_kv_heads, int32_t max_tokens) {
 size_t partial_bytes(int32_t batch, int32_t num_q_heads, int32_t splits) {
   return static_cast<size_t>(batch) * num_q_heads * splits * kPartialFloats * sizeof(float);
 }
-size_t counter_offset(int32_t batch, int32_t num_q_heads, int32_t splits) {
-  return (partial_bytes(batch, num_q_heads, splits) + 255) & ~static_cast<size_t>(255);
-}
 
 namespace {
-
-__global__ void fill_zero_u32_kernel(uint32_t* p, size_t n) {
-  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
-}
 
 oscar_status check_heads(const char* fn, int32_t batch, int32_t num_kv_heads, int32_t num_q_heads) {
   if (batch <= 0 || num_kv_heads <= 0 || num_q_heads <= 0)
@@ -187,18 +181,7 @@ size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t
   const SplitPlan pi = plan_int2(batch, num_kv_heads, max_tokens);
   const SplitPlan pb = plan_bf16(batch, num_kv_heads, max_tokens);
   const int32_t splits = pi.splits > pb.splits ? pi.splits : pb.splits;
-  return counter_offset(batch, num_q_heads, splits) + static_cast<size_t>(batch) * num_kv_heads * sizeof(uint32_t);
-}
-
-oscar_status oscar_workspace_init(void* ws, size_t ws_bytes, void* stream) {
-  const char* fn = "oscar_workspace_init";
-  if (!ws) return fail(OSCAR_EINVAL, "%s: workspace is NULL", fn);
-  if (!aligned16(ws)) return fail(OSCAR_EINVAL, "%s: workspace must be 16-byte aligned", fn);
-  const size_t n = ws_bytes / sizeof(uint32_t);
-  if (n == 0) return ok();
-  oscar_status st = check_device(fn);
-  if (st != OSCAR_OK) return st;
-  return launched(launch_fill_zero_u32(static_cast<uint32_t*>(ws), n, static_cast<hipStream_t>(stream)), fn);
+  return partial_bytes(batch, num_q_heads, splits);
 }
 
 oscar_status oscar_decode_attn(const oscar_kv_cache* cache, const int32_t* n_quant, const int32_t* n_tail,
@@ -229,11 +212,7 @@ oscar_status oscar_decode_attn(const oscar_kv_cache* cache, const int32_t* n_qua
   a.n_quant = n_quant;
   a.n_tail = n_tail;
   a.q = q;
-  a.out = out;
   a.partials = static_cast<float*>(ws);
-  const SplitPlan pb = plan_bf16(cache->batch, cache->num_kv_heads, max_tokens);
-  const int32_t ws_splits = p.splits > pb.splits ? p.splits : pb.splits;
-  a.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + counter_offset(cache->batch, num_q_heads, ws_splits));
   a.num_kv_heads = cache->num_kv_heads;
   a.num_q_heads = num_q_heads;
   a.capacity = cache->capacity;
@@ -241,7 +220,9 @@ oscar_status oscar_decode_attn(const oscar_kv_cache* cache, const int32_t* n_qua
   a.tokens_per_split = p.tokens_per_split;
   a.splits = p.splits;
   a.sm_scale = sm_scale;
-  return launched(launch_decode_int2(a, cache->batch, static_cast<hipStream_t>(stream)), fn);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = launched(launch_decode_int2(a, cache->batch, s), fn)) != OSCAR_OK) return st;
+  return launched(launch_merge(a.partials, out, cache->batch, cache->num_kv_heads, num_q_heads, p.splits, s), fn);
 }
 
 oscar_status oscar_decode_attn_bf16(const uint16_t* k, const uint16_t* v, int32_t batch, int32_t num_kv_heads,
@@ -261,16 +242,12 @@ oscar_status oscar_decode_attn_bf16(const uint16_t* k, const uint16_t* v, int32_
   if (ws_bytes < need) return fail(OSCAR_EWORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, ws_bytes, need);
   if ((st = check_device(fn)) != OSCAR_OK) return st;
   const SplitPlan p = plan_bf16(batch, num_kv_heads, max_tokens);
-  const SplitPlan pi = plan_int2(batch, num_kv_heads, max_tokens);
-  const int32_t ws_splits = p.splits > pi.splits ? p.splits : pi.splits;
   DecodeBf16Args a;
   a.k = k;
   a.v = v;
   a.seq_len = seq_len;
   a.q = q;
-  a.out = out;
   a.partials = static_cast<float*>(ws);
-  a.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + counter_offset(batch, num_q_heads, ws_splits));
   a.num_kv_heads = num_kv_heads;
   a.num_q_heads = num_q_heads;
   a.capacity = capacity;
@@ -278,16 +255,10 @@ oscar_status oscar_decode_attn_bf16(const uint16_t* k, const uint16_t* v, int32_
   a.tokens_per_split = p.tokens_per_split;
   a.splits = p.splits;
   a.sm_scale = sm_scale;
-  return launched(launch_decode_bf16(a, batch, static_cast<hipStream_t>(stream)), fn);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = launched(launch_decode_bf16(a, batch, s), fn)) != OSCAR_OK) return st;
+  return launched(launch_merge(a.partials, out, batch, num_kv_heads, num_q_heads, p.splits, s), fn);
 }
 
 }  // extern "C"
 
-namespace oscar {
-hipError_t launch_fill_zero_u32(uint32_t* p, size_t n, hipStream_t s) {
-  const unsigned threads = 256;
-  const size_t blocks = (n + threads - 1) / threads;
-  hipLaunchKernelGGL(fill_zero_u32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, s, p, n);
-  return hipGetLastError();
-}
-}  // namespace oscar

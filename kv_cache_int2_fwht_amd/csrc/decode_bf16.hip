@@ -5,7 +5,7 @@
 //
 // Same skeleton as the INT2 kernel: grid (split, KV head, sequence), 4 waves
 // per workgroup, 128-token chunks per wave with a base-2 online softmax,
-// in-LDS wave merge and a last-workgroup merge of the splits.
+// in-LDS wave merge and a per-split partial record merged by merge.hip.
 #include "decode_common.hpp"
 
 namespace oscar {
@@ -14,16 +14,18 @@ namespace {
 template <int G>
 struct Bf16Smem {
   float q_raw[G][kHeadDim];
-  float q_rot[G][kHeadDim];  // unused here; load_and_rotate_q fills both
   float pv[kDecodeWaves][G][kGroup];
-  MergeSmem<G> merge;
+  MergeSmem<G, kDecodeWaves> merge;
 };
 
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+// Per-wave state of G heads: m, l uniform across the wave; each lane owns
+// channels 2*lane and 2*lane + 1 of acc.
+template <int G>
+struct WaveState {
+  float m[G];
+  float l[G];
+  float acc[G][2];
+};
 
 template <int G>
 __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeBf16Args a) {
@@ -41,8 +43,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeBf16A
   const int t_end = min(t_begin + a.tokens_per_split, len);
   const size_t slice = static_cast<size_t>(b) * a.num_kv_heads + h;
   const int qh0 = h * G;
-  load_and_rotate_q<G>(a.q + (static_cast<size_t>(b) * a.num_q_heads + qh0) * kHeadDim, a.sm_scale * kLog2e,
-                       sm.q_raw, sm.q_rot);
+  load_and_rotate_q<G, G>(a.q + (static_cast<size_t>(b) * a.num_q_heads + qh0) * kHeadDim, a.sm_scale * kLog2e,
+                          sm.q_raw, nullptr);
 
   WaveState<G> st;
 #pragma unroll
@@ -126,9 +128,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeBf16A
     wave_sync_lds();
   }
 
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    sm.merge.acc[wave][hh][2 * lane] = st.acc[hh][0];
+    sm.merge.acc[wave][hh][2 * lane + 1] = st.acc[hh][1];
+    if (lane == 0) {
+      sm.merge.m[wave][hh] = st.m[hh];
+      sm.merge.l[wave][hh] = st.l[hh];
+    }
+  }
   const size_t partial_base = (static_cast<size_t>(b) * a.num_q_heads + qh0) * a.splits;
-  finish_split<G>(st, sm.merge, a.partials, a.counters + slice,
-                  a.out + (static_cast<size_t>(b) * a.num_q_heads + qh0) * kHeadDim, partial_base, split, a.splits);
+  write_partial<G, kDecodeWaves>(sm.merge, a.partials, partial_base, split, a.splits);
 }
 
 template <int G>

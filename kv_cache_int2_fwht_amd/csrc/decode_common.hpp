@@ -1,6 +1,6 @@
 // Split-K pieces shared by the INT2 and bf16 decode kernels: query rotation,
 // the in-workgroup merge of per-wave softmax states, the partial record and
-// the last-arriving-workgroup merge across splits.
+// the per-split partial record (merged by merge.hip).
 //
 // Softmax states are kept in base 2: logits are pre-multiplied by log2(e),
 // m is the running maximum of those scaled logits, l = sum 2^(x - m), and
@@ -17,18 +17,20 @@ constexpr int kDecodeThreads = 256;
 constexpr int kDecodeWaves = kDecodeThreads / kWave;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// q [G][128] (bf16) -> dst_raw = q * scale, dst_rot = (H q) * scale with the
-// orthonormal Sylvester Hadamard matrix (butterflies in LDS).  Block-wide.
-template <int G>
+// q [G][128] (bf16) -> dst_raw = q * scale and, if dst_rot is given,
+// dst_rot = (H q) * scale with the orthonormal Sylvester Hadamard matrix
+// (butterflies in LDS).  Rows G .. rows-1 of both are zero-filled.  Block-wide.
+template <int G, int kRows>
 __device__ void load_and_rotate_q(const uint16_t* q, float scale, float (*dst_raw)[kHeadDim],
                                   float (*dst_rot)[kHeadDim]) {
   const int tid = threadIdx.x;
-  for (int i = tid; i < G * kHeadDim; i += kDecodeThreads) {
-    const float v = bf16_to_f32(q[i]);
+  for (int i = tid; i < kRows * kHeadDim; i += kDecodeThreads) {
+    const float v = (i < G * kHeadDim) ? bf16_to_f32(q[i]) : 0.f;
     dst_raw[i / kHeadDim][i % kHeadDim] = v * scale;
-    dst_rot[i / kHeadDim][i % kHeadDim] = v;
+    if (dst_rot) dst_rot[i / kHeadDim][i % kHeadDim] = v;
   }
   __syncthreads();
+  if (!dst_rot) return;
   for (int bit = 1; bit < kHeadDim; bit <<= 1) {
     for (int i = tid; i < G * kHeadDim / 2; i += kDecodeThreads) {
       const int hh = i / (kHeadDim / 2);
@@ -46,55 +48,46 @@ __device__ void load_and_rotate_q(const uint16_t* q, float scale, float (*dst_ra
   __syncthreads();
 }
 
-// Per-wave state of G heads: m, l uniform across the wave; each lane owns
-// channels 2*lane and 2*lane + 1 of acc.
-template <int G>
-struct WaveState {
-  float m[G];
-  float l[G];
-  float acc[G][2];
-};
-
-template <int G>
+// Softmax states of G heads from kSlots producers (waves, plus extra slots
+// such as a bf16-tail state) of one workgroup.  A producer that saw no
+// token leaves m = -inf, l = 0, acc = 0.
+template <int G, int kSlots>
 struct MergeSmem {
-  float m[kDecodeWaves][G];
-  float l[kDecodeWaves][G];
-  float acc[kDecodeWaves][G][kHeadDim];
-  bool last;
+  float m[kSlots][G];
+  float l[kSlots][G];
+  float acc[kSlots][G][kHeadDim];
 };
 
-// Merge the waves' states inside the workgroup, write this split's partial
-// records, and let the last workgroup of the (sequence, KV head) merge every
-// split into out.  Must be reached by all threads of the block.
-template <int G>
-__device__ void finish_split(const WaveState<G>& st, MergeSmem<G>& sm, float* partials, uint32_t* counter,
-                             float* out_bh, size_t partial_base, int split, int splits) {
+template <int G, int kSlots>
+__device__ void clear_slot(MergeSmem<G, kSlots>& sm, int slot) {
+  // called by one wave
+  const int lane = threadIdx.x & 63;
+  for (int i = lane; i < G * kHeadDim; i += kWave) sm.acc[slot][i / kHeadDim][i % kHeadDim] = 0.f;
+  if (lane < G) {
+    sm.m[slot][lane] = -INFINITY;
+    sm.l[slot][lane] = 0.f;
+  }
+}
+
+// Merge the slots and write this split's partial records
+// partials[(partial_base + hh * splits + split) * 132] = (m, l, -, -, acc[128]).
+// Must be reached by all threads of the block after the slots are written.
+// The records of all splits are merged by merge_splits_kernel, launched
+// after the decode kernel on the same stream.
+template <int G, int kSlots>
+__device__ void write_partial(MergeSmem<G, kSlots>& sm, float* partials, size_t partial_base, int split,
+                              int splits) {
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  if (lane == 0) {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      sm.m[wave][hh] = st.m[hh];
-      sm.l[wave][hh] = st.l[hh];
-    }
-  }
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    sm.acc[wave][hh][2 * lane] = st.acc[hh][0];
-    sm.acc[wave][hh][2 * lane + 1] = st.acc[hh][1];
-  }
   __syncthreads();
-  // partial record of head hh at partials[(partial_base + hh * splits + split) * 132]
   for (int i = tid; i < G * kHeadDim; i += kDecodeThreads) {
     const int hh = i / kHeadDim;
     const int d = i % kHeadDim;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, sm.m[w][hh]);
+    for (int w = 0; w < kSlots; ++w) M = fmaxf(M, sm.m[w][hh]);
     float Lsum = 0.f, A = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
+    for (int w = 0; w < kSlots; ++w) {
       const float f = (sm.m[w][hh] == -INFINITY) ? 0.f : exp2f(sm.m[w][hh] - M);
       Lsum += sm.l[w][hh] * f;
       A += sm.acc[w][hh][d] * f;
@@ -106,35 +99,100 @@ __device__ void finish_split(const WaveState<G>& st, MergeSmem<G>& sm, float* pa
       rec[1] = Lsum;
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = atomicAdd(counter, 1u);
-    sm.last = (prev == static_cast<uint32_t>(splits - 1));
-  }
-  __syncthreads();
-  if (!sm.last) return;
-  __threadfence();
-  for (int i = tid; i < G * kHeadDim; i += kDecodeThreads) {
-    const int hh = i / kHeadDim;
-    const int d = i % kHeadDim;
-    const float* base = partials + (partial_base + static_cast<size_t>(hh) * splits) * kPartialFloats;
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, base[s * kPartialFloats]);
-    float Lsum = 0.f, A = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < splits; ++s) {
-        const float* rec = base + s * kPartialFloats;
-        const float ms = rec[0];
-        if (ms == -INFINITY) continue;
-        const float f = exp2f(ms - M);
-        Lsum += rec[1] * f;
-        A += rec[4 + d] * f;
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every
+// lane of the row receives the result.
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_f32<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_f32<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_f32<kDppRowRor4>(x));
+  x = fmaxf(x, dpp_f32<kDppRowRor8>(x));
+  return x;
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_f32<kDppQuadXor1>(x);
+  x += dpp_f32<kDppQuadXor2>(x);
+  x += dpp_f32<kDppRowRor4>(x);
+  x += dpp_f32<kDppRowRor8>(x);
+  return x;
+}
+
+// bf16 tokens (the not yet quantized tail) with plain VALU arithmetic: one
+// wave scores up to 128 tokens with the unrotated query (lane = token) and
+// accumulates their values (lane = channel pair), leaving a softmax state in
+// `slot` of the merge buffer.  k, v: token-major bf16 rows of 128 channels.
+template <int G, int kSlots>
+__device__ void bf16_tokens_wave(const uint16_t* k, const uint16_t* v, int n_tok, const float (*q_raw)[kHeadDim],
+                                 float (*pv)[kGroup], MergeSmem<G, kSlots>& sm, int slot) {
+  const int lane = threadIdx.x & 63;
+  float logit[G][2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int tt = lane + 64 * kk;
+    const bool valid = tt < n_tok;
+    float dot[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) dot[hh] = 0.f;
+    if (valid) {
+      const uint4* kr = reinterpret_cast<const uint4*>(k + static_cast<size_t>(tt) * kHeadDim);
+#pragma unroll 4
+      for (int c = 0; c < 16; ++c) {
+        const uint4 w = kr[c];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float k0 = bf16lo_to_f32(ws[e]), k1 = bf16hi_to_f32(ws[e]);
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            dot[hh] = fmaf(q_raw[hh][8 * c + 2 * e], k0, dot[hh]);
+            dot[hh] = fmaf(q_raw[hh][8 * c + 2 * e + 1], k1, dot[hh]);
+          }
+        }
       }
     }
-    out_bh[hh * kHeadDim + d] = (Lsum > 0.f) ? A / Lsum : 0.f;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) logit[hh][kk] = valid ? dot[hh] : -INFINITY;
   }
-  if (tid == 0) atomicExch(counter, 0u);
+  float mx[G], lsum[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    mx[hh] = wave_max(fmaxf(logit[hh][0], logit[hh][1]));
+    const float p0 = (mx[hh] == -INFINITY) ? 0.f : exp2f(logit[hh][0] - mx[hh]);
+    const float p1 = (mx[hh] == -INFINITY) ? 0.f : exp2f(logit[hh][1] - mx[hh]);
+    lsum[hh] = wave_sum(p0 + p1);
+    pv[hh][lane] = p0;
+    pv[hh][lane + 64] = p1;
+  }
+  wave_sync_lds();
+  float add[G][2];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) add[hh][0] = add[hh][1] = 0.f;
+  for (int tt = 0; tt < n_tok; ++tt) {
+    const uint32_t vv = *reinterpret_cast<const uint32_t*>(v + static_cast<size_t>(tt) * kHeadDim + 2 * lane);
+    const float v0 = bf16lo_to_f32(vv), v1 = bf16hi_to_f32(vv);
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float p = pv[hh][tt];
+      add[hh][0] = fmaf(p, v0, add[hh][0]);
+      add[hh][1] = fmaf(p, v1, add[hh][1]);
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    sm.acc[slot][hh][2 * lane] = add[hh][0];
+    sm.acc[slot][hh][2 * lane + 1] = add[hh][1];
+    if (lane == 0) {
+      sm.m[slot][hh] = mx[hh];
+      sm.l[slot][hh] = lsum[hh];
+    }
+  }
 }
 
 }  // namespace oscar

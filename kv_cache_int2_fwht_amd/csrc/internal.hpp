@@ -24,10 +24,8 @@ SplitPlan plan_bf16(int32_t batch, int32_t num_kv_heads, int32_t max_tokens);
 // words, acc[128]; 132 floats = 528 bytes (16-byte aligned).
 constexpr int kPartialFloats = 132;
 
-// Workspace layout: partials [batch][num_q_heads][splits][132] floats, then
-// counters [batch][num_kv_heads] uint32 at a 256-byte aligned offset.
+// Workspace layout: partials [batch][num_q_heads][splits][132] floats.
 size_t partial_bytes(int32_t batch, int32_t num_q_heads, int32_t splits);
-size_t counter_offset(int32_t batch, int32_t num_q_heads, int32_t splits);
 
 struct QuantizeArgs {
   uint8_t* k_codes;
@@ -55,9 +53,7 @@ struct DecodeInt2Args {
   const int32_t* n_quant;
   const int32_t* n_tail;
   const uint16_t* q;
-  float* out;
   float* partials;
-  uint32_t* counters;
   int32_t num_kv_heads;
   int32_t num_q_heads;
   int32_t capacity;
@@ -72,9 +68,7 @@ struct DecodeBf16Args {
   const uint16_t* v;
   const int32_t* seq_len;
   const uint16_t* q;
-  float* out;
   float* partials;
-  uint32_t* counters;
   int32_t num_kv_heads;
   int32_t num_q_heads;
   int32_t capacity;
@@ -87,6 +81,7 @@ struct DecodeBf16Args {
 hipError_t launch_quantize(const QuantizeArgs& a, int32_t batch, int32_t max_groups, hipStream_t s);
 hipError_t launch_decode_int2(const DecodeInt2Args& a, int32_t batch, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeBf16Args& a, int32_t batch, hipStream_t s);
-hipError_t launch_fill_zero_u32(uint32_t* p, size_t n, hipStream_t s);
+hipError_t launch_merge(const float* partials, float* out, int32_t batch, int32_t num_kv_heads,
+                        int32_t num_q_heads, int32_t splits, hipStream_t s);
 
 }  // namespace oscar

@@ -21,9 +21,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr double kSqrt128 = 0x1.6a09e667f3bcdp+3;  // 8 * sqrt(2)
 
-__device__ __forceinline__ uint32_t code_from(double x, double z, double inv_s) {
+__device__ __forceinline__ uint32_t code_from(double x, double z, double s, double inv_s) {
   // inv_s == 0 encodes s == 0: r = 0 and the code is 0.
-  const double r = (x - z) * inv_s;
+  double r = (x - z) * inv_s;
+  // Within a hair of a half-way point the reciprocal product can land on the
+  // other side of an exact tie; decide those with the correctly rounded quotient.
+  if (fabs((r - floor(r)) - 0.5) < 1e-9 && s > 0.0) r = (x - z) / s;
   const double c = fmin(fmax(rint(r), 0.0), 3.0);
   return static_cast<uint32_t>(c);
 }
@@ -49,8 +52,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kv_kernel(QuantizeArgs a) {
   __shared__ double red_min[16][kHeadDim];
   __shared__ double red_max[16][kHeadDim];
   __shared__ double zs[kHeadDim];
+  __shared__ double ss[kHeadDim];
   __shared__ double inv_s[kHeadDim];
   __shared__ double vz[kGroup];
+  __shared__ double vs[kGroup];
   __shared__ double vinv[kGroup];
 
   // ---------------- keys ----------------
@@ -145,6 +150,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kv_kernel(QuantizeArgs a) {
         static_cast<uint32_t>(s_bits) | (static_cast<uint32_t>(z_bits) << 16);
     const double s16 = f16_bits_to_f64(s_bits);
     zs[tid] = f16_bits_to_f64(z_bits);
+    ss[tid] = s16;
     inv_s[tid] = (s16 > 0.0) ? 1.0 / s16 : 0.0;
   }
   __syncthreads();
@@ -154,8 +160,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kv_kernel(QuantizeArgs a) {
     uint32_t w0 = 0, w1 = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      w0 |= code_from(u[pass][i], zs[32 * L + i], inv_s[32 * L + i]) << (2 * i);
-      w1 |= code_from(u[pass][16 + i], zs[32 * L + 16 + i], inv_s[32 * L + 16 + i]) << (2 * i);
+      w0 |= code_from(u[pass][i], zs[32 * L + i], ss[32 * L + i], inv_s[32 * L + i]) << (2 * i);
+      w1 |= code_from(u[pass][16 + i], zs[32 * L + 16 + i], ss[32 * L + 16 + i], inv_s[32 * L + 16 + i]) << (2 * i);
     }
     *reinterpret_cast<uint2*>(a.k_codes + (tok0 + t) * 32 + 8 * L) = make_uint2(w0, w1);
     if (L == 0) a.k_norm[tok0 + t] = n16_bits[pass];
@@ -193,6 +199,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kv_kernel(QuantizeArgs a) {
             static_cast<uint32_t>(s_bits) | (static_cast<uint32_t>(z_bits) << 16);
         const double s16 = f16_bits_to_f64(s_bits);
         vz[t] = f16_bits_to_f64(z_bits);
+        vs[t] = s16;
         vinv[t] = (s16 > 0.0) ? 1.0 / s16 : 0.0;
       }
     }
@@ -210,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kv_kernel(QuantizeArgs a) {
       for (int e = 0; e < 16; ++e) {
         const int t = half * 64 + wd * 16 + e;
         const double v = static_cast<double>(bf16_to_f32(vsrc[static_cast<int64_t>(t) * a.st + d]));
-        acc |= code_from(v, vz[t], vinv[t]) << (2 * e);
+        acc |= code_from(v, vz[t], vs[t], vinv[t]) << (2 * e);
       }
       words[wd] = acc;
     }

@@ -28,7 +28,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     L = ob.lib()
     declared = _declared_functions()
-    assert len(declared) >= 8
+    assert len(declared) >= 7
     for name in declared:
         assert hasattr(L, name), f"{name} declared in oscar.h but not exported"
     assert set(declared) == set(ob.EXPORTED)
@@ -48,9 +48,9 @@ def test_workspace_size_rules():
     assert f(1, 8, 32, -1) == 0
     small, big = f(1, 8, 32, 8192), f(1, 8, 32, 131072)
     assert 0 < small <= big
-    assert f(1, 8, 32, 0) > 0              # an empty cache still needs the counters
-    # counters sit at the end, 4 bytes per (sequence, KV head)
-    assert f(8, 8, 32, 131072) >= 8 * 8 * 4
+    assert f(1, 8, 32, 0) > 0              # an empty cache still gets one (empty) split
+    # one 528-byte partial record per (sequence, query head, split) at least
+    assert f(8, 8, 32, 131072) >= 8 * 32 * 528
 
 
 def _no_gpu():

@@ -104,9 +104,6 @@ def test_int2_decode_empty_and_deterministic(gpu_lib):
     b, _ = _run_int2(ob, cache, q, lens, nq, dev)
     assert np.array_equal(a, b)
     assert np.all(a[0] == 0.0)
-    # the workspace's arrival counters are back at zero after every call
-    counters = ws[-(w.batch * w.num_kv_heads) * 4:].view(torch.int32)
-    assert int(counters.abs().sum()) == 0
 
 
 @pytest.mark.parametrize("case", ["cfg0", "cfg1", "ragged_g4", "g8"])

@@ -51,8 +51,11 @@ oscar_status launched(hipError_t e, const char* fn) {
 
 // About two workgroups per compute unit: each wave then streams several
 // groups back to back (prefetching the next while computing the current).
-constexpr int64_t kTargetBlocks = 512;
-constexpr int64_t kMinBlocks = 512;
+#ifndef OSCAR_TARGET_BLOCKS
+#define OSCAR_TARGET_BLOCKS 512
+#endif
+constexpr int64_t kTargetBlocks = OSCAR_TARGET_BLOCKS;
+constexpr int64_t kMinBlocks = OSCAR_TARGET_BLOCKS;
 
 SplitPlan make_plan(int32_t batch, int32_t num_kv_heads, int32_t max_tokens) {
   const int64_t heads = static_cast<int64_t>(batch) * num_kv_heads;

@@ -23,11 +23,15 @@
 // Work split: grid (split, KV head, sequence); 4 waves per workgroup; each
 // wave streams whole 128-token groups (prefetching the next group's bytes
 // while computing the current one) with a base-2 online softmax.  Lane
-// roles inside a wave (lane = 16 * r + n):
-//  * score / softmax lane (r, n): head r of the row block, tokens 8n .. 8n+7
-//    of the group (one per 16-token column tile i, token 8n + i);
-//  * q' lane (r, n): head r, channels 8n .. 8n+7;
+// roles inside a wave (lane = 16 * r + n, w = n >> 1, u = 2 (n & 1)):
+//  * score / softmax lane (r, n): head r of the row block, the tokens
+//    16w + 4b + u + c of the group (b = 0..3, c = 0..1; column n of tile
+//    4c + b);
+//  * q' lane (r, n): head r, the channels 16w + 4b + u + c;
 //  * value lane (r, n): head r, channels 16j + n of channel tile j.
+// With these sets, the four digits of the values a lane owns for one c land
+// in four consecutive bytes of one MFMA operand row, so each lane stages
+// its operand bytes with one 8-byte LDS write per digit row.
 // The waves merge in LDS into one partial record per split; merge.hip
 // combines the splits.
 #include "decode_common.hpp"
@@ -67,46 +71,70 @@ __device__ __forceinline__ float digits_value(const v4i& c) {
 }
 
 struct GroupBytes {
-  uint2 kd[8];    // K codes of token 8n + i, dwords 2g and 2g+1 of the row (g = lane >> 4)
-  uint2 vd[8];    // V codes of channel 16j + n, dwords 2g and 2g+1 of the channel row
-  uint4 norm;     // fp16 norms of tokens 8n .. 8n+7
-  uint4 vsz[2];   // (vs, vz) fp16 pairs of tokens 8n .. 8n+7
-  uint4 ksz[2];   // (s, z) fp16 pairs of channels 8n .. 8n+7
+  uint2 kd[8];     // K codes of token tau(4c+b) (see lane roles), dwords 2g and 2g+1 of the row
+  uint2 vd[8];     // V codes of channel 16j + n, dwords 2g and 2g+1 of the channel row
+  uint32_t nrm[4];  // fp16 norms of tokens 16w + 4b + u + {0, 1}
+  uint2 vsz[4];     // (vs | vz << 16) of tokens 16w + 4b + u + {0, 1}
+  uint2 ksz[4];     // (s | z << 16) of channels 16w + 4b + u + {0, 1}
 };
 
 __device__ __forceinline__ void load_group(GroupBytes& r, const DecodeInt2Args& a, size_t slice, int groups_cap,
                                            int g, int lane) {
   const int gl = lane >> 4;
   const int n = lane & 15;
+  const int base = 16 * (n >> 1) + 2 * (n & 1);   // token / channel 16w + u
   const size_t row0 = slice * a.capacity + static_cast<size_t>(g) * kGroup;   // first token row
   const size_t grp = slice * groups_cap + g;
-  const uint8_t* kc = a.k_codes + (row0 + 8 * n) * 32 + 8 * gl;
+  const uint8_t* kc = a.k_codes + (row0 + base) * 32 + 8 * gl;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r.kd[i] = *reinterpret_cast<const uint2*>(kc + i * 32);
+  for (int i = 0; i < 8; ++i) r.kd[i] = *reinterpret_cast<const uint2*>(kc + (4 * (i & 3) + (i >> 2)) * 32);
   const uint8_t* vc = a.v_codes + (grp * kHeadDim + n) * 32 + 8 * gl;
 #pragma unroll
   for (int j = 0; j < 8; ++j) r.vd[j] = *reinterpret_cast<const uint2*>(vc + j * 16 * 32);
-  r.norm = *reinterpret_cast<const uint4*>(a.k_norm + row0 + 8 * n);
-  const uint4* vs = reinterpret_cast<const uint4*>(a.v_sz + (row0 + 8 * n) * 2);
-  r.vsz[0] = vs[0];
-  r.vsz[1] = vs[1];
-  const uint4* ks = reinterpret_cast<const uint4*>(a.k_sz + (grp * kHeadDim + 8 * n) * 2);
-  r.ksz[0] = ks[0];
-  r.ksz[1] = ks[1];
-}
-
-__device__ __forceinline__ uint32_t word8(const uint4 (&w)[2], int j) {
-  const uint4 x = w[j >> 2];
-  switch (j & 3) {
-    case 0: return x.x;
-    case 1: return x.y;
-    case 2: return x.z;
-    default: return x.w;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    r.nrm[b] = *reinterpret_cast<const uint32_t*>(a.k_norm + row0 + base + 4 * b);
+    r.vsz[b] = *reinterpret_cast<const uint2*>(a.v_sz + (row0 + base + 4 * b) * 2);
+    r.ksz[b] = *reinterpret_cast<const uint2*>(a.k_sz + (grp * kHeadDim + base + 4 * b) * 2);
   }
 }
-__device__ __forceinline__ uint32_t half8(const uint4& w, int i) {  // fp16 i of 8 packed in a uint4
-  const uint32_t x = (i >> 1) == 0 ? w.x : (i >> 1) == 1 ? w.y : (i >> 1) == 2 ? w.z : w.w;
-  return (i & 1) ? (x >> 16) : (x & 0xffffu);
+
+__device__ __forceinline__ uint32_t pick(const uint2& v, int c) { return c ? v.y : v.x; }
+__device__ __forceinline__ float f16_lo(uint32_t w) { return f16_bits_to_f32(static_cast<uint16_t>(w & 0xffffu)); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return f16_bits_to_f32(static_cast<uint16_t>(w >> 16)); }
+
+// 4x4 byte transpose: y[k] byte b = x[b] byte k.
+__device__ __forceinline__ void transpose4(const uint32_t (&x)[4], uint32_t (&y)[4]) {
+  const uint32_t t01_lo = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);
+  const uint32_t t01_hi = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);
+  const uint32_t t23_lo = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
+  const uint32_t t23_hi = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);
+  y[0] = __builtin_amdgcn_perm(t23_lo, t01_lo, 0x05040100u);
+  y[1] = __builtin_amdgcn_perm(t23_lo, t01_lo, 0x07060302u);
+  y[2] = __builtin_amdgcn_perm(t23_hi, t01_hi, 0x05040100u);
+  y[3] = __builtin_amdgcn_perm(t23_hi, t01_hi, 0x07060302u);
+}
+
+// MFMA A operand staging: per (operand half or K step, lane group) a block of
+// 16 rows x 16 bytes plus 16 bytes of padding, so that the 8-byte writes of
+// a wave spread over all LDS banks.
+constexpr int kOpRow = 16;
+constexpr int kOpBlock = 16 * kOpRow + 16;
+
+// Write the digit rows of the eight fixed-point values x[c][b] a lane owns
+// (c = 0..1, b = 0..3) into operand block `blk` (a pointer to [2][4][kOpBlock]).
+__device__ __forceinline__ void stage_digits(uint8_t* blk, const uint32_t (&x)[2][4], int gl, int n) {
+  uint32_t y0[4], y1[4];
+  transpose4(x[0], y0);
+  transpose4(x[1], y1);
+  const int w = n >> 1;
+  uint8_t* dst = blk + ((w & 1) * 4 + (w >> 1)) * kOpBlock + 8 * (n & 1);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) *reinterpret_cast<uint2*>(dst + (4 * gl + k) * kOpRow) = make_uint2(y0[k], y1[k]);
+}
+
+__device__ __forceinline__ v4i read_operand(const uint8_t* blk, int half, int gl, int n) {
+  return *reinterpret_cast<const v4i*>(blk + (half * 4 + gl) * kOpBlock + n * kOpRow);
 }
 
 template <int G>
@@ -124,10 +152,145 @@ struct Int2Smem {
     float tail_p[G][kGroup];                    // softmax weights of the bf16 tail tokens
   } u;
   // per wave and row block: MFMA A operands staged as [half][lane group][row][16 bytes]
-  uint8_t a_qk[kDecodeWaves][Int2Cfg<G>::kRB][2][4][16][16];
-  uint8_t a_pv[kDecodeWaves][Int2Cfg<G>::kRB][2][4][16][16];
+  uint8_t a_qk[kDecodeWaves][Int2Cfg<G>::kRB][2 * 4 * kOpBlock];
+  uint8_t a_pv[kDecodeWaves][Int2Cfg<G>::kRB][2 * 4 * kOpBlock];
   MergeSmem<G, Int2Cfg<G>::kSlots> merge;
 };
+
+// Running softmax state of one wave: per row block, m (uniform over the
+// head's 16 lanes), per-lane partial l and sum p * vz, and acc for channels
+// 16j + n.
+template <int RB>
+struct WaveRun {
+  float m[RB], l[RB], z[RB], acc[RB][8];
+};
+
+// One quantized 128-token group: scores on the matrix cores, online softmax,
+// weighted value codes on the matrix cores.
+template <int G>
+__device__ __forceinline__ void process_group(const GroupBytes& cur, int t0, int t_end,
+                                              const float (&qv)[Int2Cfg<G>::kRB][2][4], const float (&fac)[2],
+                                              Int2Smem<G>& sm, WaveRun<Int2Cfg<G>::kRB>& st, int wave, int gl,
+                                              int n) {
+  constexpr int RB = Int2Cfg<G>::kRB;
+  const int tok_base = t0 + 16 * (n >> 1) + 2 * (n & 1);
+  // ---- q' = Hq * s16 as 4-digit fixed point (A operand), Z = Hq . z16 ----
+  float Zg[RB], inv_q[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float qs[2][4];
+    float zp = 0.f, amax = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint32_t w = pick(cur.ksz[b], c);
+        qs[c][b] = qv[rb][c][b] * f16_lo(w);
+        zp = fmaf(qv[rb][c][b], f16_hi(w), zp);
+        amax = fmaxf(amax, fabsf(qs[c][b]));
+      }
+    amax = row_max16(amax);
+    Zg[rb] = row_sum16(zp);
+    int e;
+    frexpf(amax, &e);                        // amax < 2^e
+    const float sc = ldexpf(1.f, 26 - e);    // |q' * sc| < 2^26
+    inv_q[rb] = ldexpf(1.f, e - 30);         // 1 / (sc * 16)
+    uint32_t x[2][4];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) x[c][b] = balanced_digits(static_cast<int>(rintf(qs[c][b] * (sc * fac[c]))));
+    stage_digits(sm.a_qk[wave][rb], x, gl, n);
+  }
+  wave_sync_lds();
+  v4i aq[RB][2];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    aq[rb][0] = read_operand(sm.a_qk[wave][rb], 0, gl, n);
+    aq[rb][1] = read_operand(sm.a_qk[wave][rb], 1, gl, n);
+  }
+
+  // ---- scores: column n of tile i = 4c + b is token 16w + 4b + u + c ----
+  float logit[RB][2][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = i >> 2, b = i & 3;
+    const v4i b0 = spread_codes(cur.kd[i].x);
+    const v4i b1 = spread_codes(cur.kd[i].y);
+    const float n16 = c ? f16_hi(cur.nrm[b]) : f16_lo(cur.nrm[b]);
+    const bool valid = tok_base + 4 * b + c < t_end;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      v4i acc = {0, 0, 0, 0};
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[rb][0], b0, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[rb][1], b1, acc, 0, 0, 0);
+      logit[rb][c][b] = valid ? n16 * fmaf(digits_value(acc), inv_q[rb], Zg[rb]) : -INFINITY;
+    }
+  }
+
+  // ---- online softmax (base 2) and p * vs as 4-digit fixed point ----
+  float inv_p[RB], alpha[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float gm = logit[rb][0][0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) gm = fmaxf(gm, logit[rb][i >> 2][i & 3]);
+    gm = row_max16(gm);
+    const float m_new = fmaxf(st.m[rb], gm);   // finite: every group has a valid token
+    alpha[rb] = (st.m[rb] == -INFINITY) ? 0.f : exp2f(st.m[rb] - m_new);
+    st.m[rb] = m_new;
+    float ls = 0.f, zs = 0.f, pmax = 0.f;
+    float pv[2][4];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t w = pick(cur.vsz[b], c);
+        const float p = exp2f(logit[rb][c][b] - m_new);
+        ls += p;
+        zs = fmaf(p, f16_hi(w), zs);
+        pv[c][b] = p * f16_lo(w);
+        pmax = fmaxf(pmax, pv[c][b]);
+      }
+    st.l[rb] = fmaf(st.l[rb], alpha[rb], ls);
+    st.z[rb] = fmaf(st.z[rb], alpha[rb], zs);
+    pmax = row_max16(pmax);
+    int e2;
+    frexpf(pmax, &e2);                       // p * vs < 2^e2 for this head and group
+    const float sc2 = ldexpf(1.f, 26 - e2);
+    inv_p[rb] = ldexpf(1.f, e2 - 30);
+    uint32_t x[2][4];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)   // p * vs >= 0: +0.5 then truncation rounds to nearest
+        x[c][b] = balanced_digits(static_cast<int>(fmaf(pv[c][b], sc2 * fac[c], 0.5f)));
+    stage_digits(sm.a_pv[wave][rb], x, gl, n);
+  }
+  wave_sync_lds();
+  v4i ap[RB][2];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    ap[rb][0] = read_operand(sm.a_pv[wave][rb], 0, gl, n);
+    ap[rb][1] = read_operand(sm.a_pv[wave][rb], 1, gl, n);
+  }
+
+  // ---- weighted value codes: channel tile j, column n = channel 16j + n ----
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const v4i b0 = spread_codes(cur.vd[j].x);
+    const v4i b1 = spread_codes(cur.vd[j].y);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      v4i acc = {0, 0, 0, 0};
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap[rb][0], b0, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap[rb][1], b1, acc, 0, 0, 0);
+      st.acc[rb][j] = fmaf(digits_value(acc), inv_p[rb], st.acc[rb][j] * alpha[rb]);
+    }
+  }
+  // the next group rewrites a_qk / a_pv only after this wave has read them
+  wave_sync_lds();
+}
 
 template <int G>
 __global__ __launch_bounds__(kDecodeThreads) void decode_int2_kernel(DecodeInt2Args a) {
@@ -156,173 +319,63 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_int2_kernel(DecodeInt2A
   const size_t slice = static_cast<size_t>(b) * a.num_kv_heads + h;
   const int qh0 = h * G;
 
-  if (wave == 0) clear_slot(sm.merge, kDecodeWaves);  // the tail slot stays empty unless a tail is seen
-  load_and_rotate_q<G, C::kRows>(a.q + (static_cast<size_t>(b) * a.num_q_heads + qh0) * kHeadDim,
-                                 a.sm_scale * kLog2e, sm.q_raw, sm.u.q_rot);
-
-  // rotated query of this lane's head and channels 8n .. 8n+7, per row block
-  float qv[RB][8];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) qv[rb][j] = sm.u.q_rot[rb * 4 + gl][8 * n + j];
-  __syncthreads();  // q_rot shares storage with tail_p
-
-  float m_run[RB], l_run[RB], z_run[RB], acc[RB][8];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = -INFINITY;
-    l_run[rb] = 0.f;
-    z_run[rb] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[rb][j] = 0.f;
-  }
-
   const int g_begin = t_begin / kGroup;
   const int g_end = (t_end + kGroup - 1) / kGroup;
   const int g_qend = min(g_end, nq / kGroup);   // quantized groups end here; a tail group may follow
   int g = g_begin + wave;
-  GroupBytes cur, nxt;
-  if (g < g_qend) load_group(cur, a, slice, groups_cap, g, lane);
-  for (; g < g_qend; g += kDecodeWaves) {
-    const int g_next = g + kDecodeWaves;
-    if (g_next < g_qend) load_group(nxt, a, slice, groups_cap, g_next, lane);
-    const int t0 = g * kGroup;
+  // start streaming this wave's first group before the query set-up
+  GroupBytes buf0, buf1;
+  if (g < g_qend) load_group(buf0, a, slice, groups_cap, g, lane);
 
-    // ---- q' = Hq * s16 as 4-digit fixed point (A operand), Z = Hq . z16 ----
-    float Zg[RB], inv_q[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float qs[8];
-      float zp = 0.f, amax = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t w = word8(cur.ksz, j);
-        const float s = f16_bits_to_f32(static_cast<uint16_t>(w & 0xffffu));
-        const float z = f16_bits_to_f32(static_cast<uint16_t>(w >> 16));
-        qs[j] = qv[rb][j] * s;
-        zp = fmaf(qv[rb][j], z, zp);
-        amax = fmaxf(amax, fabsf(qs[j]));
-      }
-      amax = row_max16(amax);
-      Zg[rb] = row_sum16(zp);
-      int e;
-      frexpf(amax, &e);                        // amax < 2^e
-      const float sc = ldexpf(1.f, 26 - e);    // |q' * sc| < 2^26
-      inv_q[rb] = ldexpf(1.f, e - 30);         // 1 / (sc * 16)
-      uint8_t(*dst)[4][16][16] = sm.a_qk[wave][rb];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t dg = balanced_digits(static_cast<int>(qs[j] * (sc * kInvWeight16[j & 3])));
-        // channel 8n + j sits in packed dword w = n >> 1 (operand half w & 1,
-        // lane group w >> 1), byte 2 (n & 1) + (j >> 2), bit pair j & 3, i.e.
-        // operand byte 4 (j & 3) + 2 (n & 1) + (j >> 2).
-        const int half = (n >> 1) & 1, g4 = n >> 2, p = 4 * (j & 3) + 2 * (n & 1) + (j >> 2);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) dst[half][g4][4 * gl + k][p] = static_cast<uint8_t>(dg >> (8 * k));
-      }
-    }
-    wave_sync_lds();
-    v4i aq[RB][2];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      aq[rb][0] = *reinterpret_cast<const v4i*>(sm.a_qk[wave][rb][0][gl][n]);
-      aq[rb][1] = *reinterpret_cast<const v4i*>(sm.a_qk[wave][rb][1][gl][n]);
-    }
+  if (wave == 0) clear_slot(sm.merge, kDecodeWaves);  // the tail slot stays empty unless a tail is seen
+  load_and_rotate_q<G, C::kRows>(a.q + (static_cast<size_t>(b) * a.num_q_heads + qh0) * kHeadDim,
+                                 a.sm_scale * kLog2e, sm.q_raw, sm.u.q_rot);
 
-    // ---- scores of tokens 8n + i (column n of tile i) ----
-    float logit[RB][8];
+  // rotated query of this lane's head and channels 16w + 4b + u + c, per row block
+  float qv[RB][2][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const v4i b0 = spread_codes(cur.kd[i].x);
-      const v4i b1 = spread_codes(cur.kd[i].y);
-      const float n16 = f16_bits_to_f32(static_cast<uint16_t>(half8(cur.norm, i)));
-      const bool valid = t0 + 8 * n + i < t_end;
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        v4i c = {0, 0, 0, 0};
-        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[rb][0], b0, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[rb][1], b1, c, 0, 0, 0);
-        logit[rb][i] = valid ? n16 * fmaf(digits_value(c), inv_q[rb], Zg[rb]) : -INFINITY;
-      }
-    }
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) qv[rb][c][b] = sm.u.q_rot[rb * 4 + gl][16 * (n >> 1) + 4 * b + 2 * (n & 1) + c];
+  __syncthreads();  // q_rot shares storage with tail_p
+  // weight divisors of the bit pairs u + c this lane's values occupy
+  const float fac[2] = {kInvWeight16[2 * (n & 1)], kInvWeight16[2 * (n & 1) + 1]};
 
-    // ---- online softmax (base 2) and p * vs as 4-digit fixed point ----
-    float vs[8], vz[8], vmax = 0.f;
+  WaveRun<RB> st;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t w = word8(cur.vsz, i);
-      vs[i] = f16_bits_to_f32(static_cast<uint16_t>(w & 0xffffu));
-      vz[i] = f16_bits_to_f32(static_cast<uint16_t>(w >> 16));
-      vmax = fmaxf(vmax, vs[i]);
-    }
-    vmax = row_max16(vmax);
-    int e2;
-    frexpf(vmax, &e2);
-    const float sc2 = ldexpf(1.f, 26 - e2);
-    const float inv2 = ldexpf(1.f, e2 - 30);
-    float alpha[RB];
+  for (int rb = 0; rb < RB; ++rb) {
+    st.m[rb] = -INFINITY;
+    st.l[rb] = 0.f;
+    st.z[rb] = 0.f;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float gm = logit[rb][0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) gm = fmaxf(gm, logit[rb][i]);
-      gm = row_max16(gm);
-      const float m_new = fmaxf(m_run[rb], gm);   // finite: every group has a valid token
-      alpha[rb] = (m_run[rb] == -INFINITY) ? 0.f : exp2f(m_run[rb] - m_new);
-      m_run[rb] = m_new;
-      float ls = 0.f, zs = 0.f;
-      uint8_t(*dst)[4][16][16] = sm.a_pv[wave][rb];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p = exp2f(logit[rb][i] - m_new);
-        ls += p;
-        zs = fmaf(p, vz[i], zs);
-        const uint32_t dg = balanced_digits(static_cast<int>(p * vs[i] * (sc2 * kInvWeight16[i & 3])));
-        // token 8n + i sits in packed dword w = n >> 1 of its channel row
-        // (K step w & 1, lane group w >> 1), byte 2 (n & 1) + (i >> 2), bit pair i & 3.
-        const int ks = (n >> 1) & 1, g4 = n >> 2, p4 = 4 * (i & 3) + 2 * (n & 1) + (i >> 2);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) dst[ks][g4][4 * gl + k][p4] = static_cast<uint8_t>(dg >> (8 * k));
-      }
-      l_run[rb] = fmaf(l_run[rb], alpha[rb], ls);
-      z_run[rb] = fmaf(z_run[rb], alpha[rb], zs);
-    }
-    wave_sync_lds();
-    v4i ap[RB][2];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      ap[rb][0] = *reinterpret_cast<const v4i*>(sm.a_pv[wave][rb][0][gl][n]);
-      ap[rb][1] = *reinterpret_cast<const v4i*>(sm.a_pv[wave][rb][1][gl][n]);
-    }
+    for (int j = 0; j < 8; ++j) st.acc[rb][j] = 0.f;
+  }
 
-    // ---- weighted value codes: channel tile j, column n = channel 16j + n ----
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const v4i b0 = spread_codes(cur.vd[j].x);
-      const v4i b1 = spread_codes(cur.vd[j].y);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        v4i c = {0, 0, 0, 0};
-        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap[rb][0], b0, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap[rb][1], b1, c, 0, 0, 0);
-        acc[rb][j] = fmaf(digits_value(c), inv2, acc[rb][j] * alpha[rb]);
-      }
-    }
-    if (g_next < g_qend) cur = nxt;
+  // two register buffers in turn: the next group streams in while the
+  // current one is computed
+  while (g < g_qend) {
+    if (g + kDecodeWaves < g_qend) load_group(buf1, a, slice, groups_cap, g + kDecodeWaves, lane);
+    process_group<G>(buf0, g * kGroup, t_end, qv, fac, sm, st, wave, gl, n);
+    g += kDecodeWaves;
+    if (g >= g_qend) break;
+    if (g + kDecodeWaves < g_qend) load_group(buf0, a, slice, groups_cap, g + kDecodeWaves, lane);
+    process_group<G>(buf1, g * kGroup, t_end, qv, fac, sm, st, wave, gl, n);
+    g += kDecodeWaves;
   }
 
   // ---- this wave's state -> merge slot ----
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const float l_tot = row_sum16(l_run[rb]);
-    const float z_tot = row_sum16(z_run[rb]);
+    const float l_tot = row_sum16(st.l[rb]);
+    const float z_tot = row_sum16(st.z[rb]);
     const int hh = rb * 4 + gl;
     if (hh < G) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sm.merge.acc[wave][hh][16 * j + n] = acc[rb][j] + z_tot;
+      for (int j = 0; j < 8; ++j) sm.merge.acc[wave][hh][16 * j + n] = st.acc[rb][j] + z_tot;
       if (n == 0) {
-        sm.merge.m[wave][hh] = m_run[rb];
+        sm.merge.m[wave][hh] = st.m[rb];
         sm.merge.l[wave][hh] = l_tot;
       }
     }

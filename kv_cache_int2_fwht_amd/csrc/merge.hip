@@ -7,84 +7,90 @@
 // sum_s w_s acc_s / sum_s w_s l_s, with out = 0 when every split is empty.
 // The splits are combined in a fixed order, so the result is deterministic.
 //
-// One workgroup per (KV head, sequence), one wave per query head: lane s
-// reads m_s and l_s of split s, every lane reads two channels of every
-// split's acc, all loads are issued before any arithmetic waits on them.
+// One workgroup per (query head, sequence), so that the partial records are
+// read by many compute units at once.  Wave w merges the splits w, w + 4,
+// ... (lane = two channels; the record's m and l are read by every lane
+// from the same address), then wave 0 merges the four wave results.
 #include "decode_common.hpp"
 
 namespace oscar {
 namespace {
 
-constexpr int kChunk = 64;   // splits handled per pass (one per lane)
+constexpr int kMergeUnroll = 8;
 
-template <int G>
 __global__ __launch_bounds__(kDecodeThreads) void merge_splits_kernel(const float* __restrict__ partials,
                                                                        float* __restrict__ out, int num_q_heads,
                                                                        int splits) {
-  const int h = blockIdx.x;
+  const int qh = blockIdx.x;
   const int b = blockIdx.y;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  for (int hh = wave; hh < G; hh += kDecodeWaves) {
-    const int qh = h * G + hh;
-    const float* base = partials + (static_cast<size_t>(b) * num_q_heads + qh) * splits * kPartialFloats;
-    float M = -INFINITY;
-    for (int c0 = 0; c0 < splits; c0 += kChunk) {
-      const int s = c0 + lane;
-      const float ms = (s < splits) ? base[static_cast<size_t>(s) * kPartialFloats] : -INFINITY;
-      M = fmaxf(M, wave_max(ms));
-    }
-    float L = 0.f, a0 = 0.f, a1 = 0.f;
-    if (M != -INFINITY) {
-      for (int c0 = 0; c0 < splits; c0 += kChunk) {
-        const int s = c0 + lane;
-        float ms = -INFINITY, ls = 0.f;
-        if (s < splits) {
-          ms = base[static_cast<size_t>(s) * kPartialFloats];
-          ls = base[static_cast<size_t>(s) * kPartialFloats + 1];
-        }
-        const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-        L += wave_sum(ls * w);
-        const int cnt = min(kChunk, splits - c0);
-        float2 v[kChunk];
+  __shared__ float sm_m[kDecodeWaves], sm_l[kDecodeWaves];
+  __shared__ float2 sm_acc[kDecodeWaves][kWave];
+  const float* base = partials + (static_cast<size_t>(b) * num_q_heads + qh) * splits * kPartialFloats;
+
+  float M = -INFINITY, L = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int s0 = wave; s0 < splits; s0 += kDecodeWaves * kMergeUnroll) {
+    float2 ml[kMergeUnroll], v[kMergeUnroll];
 #pragma unroll
-        for (int k = 0; k < kChunk; ++k) {
-          v[k] = (k < cnt) ? *reinterpret_cast<const float2*>(base + static_cast<size_t>(c0 + k) * kPartialFloats + 4 +
-                                                              2 * lane)
-                           : make_float2(0.f, 0.f);
-        }
-#pragma unroll
-        for (int k = 0; k < kChunk; ++k) {
-          const float wk = __shfl(w, k, kWave);
-          a0 = fmaf(wk, v[k].x, a0);
-          a1 = fmaf(wk, v[k].y, a1);
-        }
+    for (int k = 0; k < kMergeUnroll; ++k) {   // all loads of the batch first
+      const int s = s0 + k * kDecodeWaves;
+      if (s < splits) {
+        const float* rec = base + static_cast<size_t>(s) * kPartialFloats;
+        ml[k] = *reinterpret_cast<const float2*>(rec);
+        v[k] = *reinterpret_cast<const float2*>(rec + 4 + 2 * lane);
+      } else {
+        ml[k] = make_float2(-INFINITY, 0.f);
+        v[k] = make_float2(0.f, 0.f);
       }
     }
-    float2 r = (L > 0.f) ? make_float2(a0 / L, a1 / L) : make_float2(0.f, 0.f);
-    *reinterpret_cast<float2*>(out + (static_cast<size_t>(b) * num_q_heads + qh) * kHeadDim + 2 * lane) = r;
+#pragma unroll
+    for (int k = 0; k < kMergeUnroll; ++k) {
+      const float ms = ml[k].x;
+      if (ms == -INFINITY) continue;          // empty split (uniform over the wave)
+      const float M_new = fmaxf(M, ms);
+      const float r = (M == -INFINITY) ? 0.f : exp2f(M - M_new);
+      const float w = exp2f(ms - M_new);
+      L = fmaf(L, r, ml[k].y * w);
+      a0 = fmaf(a0, r, v[k].x * w);
+      a1 = fmaf(a1, r, v[k].y * w);
+      M = M_new;
+    }
   }
-}
-
-template <int G>
-hipError_t launch_g(const float* partials, float* out, int batch, int num_kv_heads, int num_q_heads, int splits,
-                    hipStream_t s) {
-  hipLaunchKernelGGL(merge_splits_kernel<G>, dim3(num_kv_heads, batch), dim3(kDecodeThreads), 0, s, partials, out,
-                     num_q_heads, splits);
-  return hipGetLastError();
+  if (lane == 0) {
+    sm_m[wave] = M;
+    sm_l[wave] = L;
+  }
+  sm_acc[wave][lane] = make_float2(a0, a1);
+  __syncthreads();
+  if (wave == 0) {
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) Mt = fmaxf(Mt, sm_m[w]);
+    float Lt = 0.f, r0 = 0.f, r1 = 0.f;
+    if (Mt != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kDecodeWaves; ++w) {
+        if (sm_m[w] == -INFINITY) continue;
+        const float f = exp2f(sm_m[w] - Mt);
+        Lt = fmaf(sm_l[w], f, Lt);
+        r0 = fmaf(sm_acc[w][lane].x, f, r0);
+        r1 = fmaf(sm_acc[w][lane].y, f, r1);
+      }
+    }
+    const float2 res = (Lt > 0.f) ? make_float2(r0 / Lt, r1 / Lt) : make_float2(0.f, 0.f);
+    *reinterpret_cast<float2*>(out + (static_cast<size_t>(b) * num_q_heads + qh) * kHeadDim + 2 * lane) = res;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_merge(const float* partials, float* out, int32_t batch, int32_t num_kv_heads, int32_t num_q_heads,
                         int32_t splits, hipStream_t s) {
-  switch (num_q_heads / num_kv_heads) {
-    case 1: return launch_g<1>(partials, out, batch, num_kv_heads, num_q_heads, splits, s);
-    case 2: return launch_g<2>(partials, out, batch, num_kv_heads, num_q_heads, splits, s);
-    case 4: return launch_g<4>(partials, out, batch, num_kv_heads, num_q_heads, splits, s);
-    case 8: return launch_g<8>(partials, out, batch, num_kv_heads, num_q_heads, splits, s);
-    default: return hipErrorInvalidValue;
-  }
+  (void)num_kv_heads;
+  hipLaunchKernelGGL(merge_splits_kernel, dim3(num_q_heads, batch), dim3(kDecodeThreads), 0, s, partials, out,
+                     num_q_heads, splits);
+  return hipGetLastError();
 }
 
 }  // namespace oscar

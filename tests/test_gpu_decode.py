@@ -106,6 +106,25 @@ def test_int2_decode_empty_and_deterministic(gpu_lib):
     assert np.all(a[0] == 0.0)
 
 
+def test_int2_decode_reused_workspace_sees_fresh_partials(gpu_lib):
+    """One workspace, many calls with different data: the split merge must
+    read this call's partial records, never a stale copy of an earlier call's."""
+    from kv_cache_int2_fwht_amd import binding as ob
+    dev = torch.device("cuda:0")
+    ws = None
+    for tag in range(108, 113):
+        w = syn.custom_workload(1, 32, 8, [6000 + 37 * (tag - 108)], cfg_tag=tag)
+        cache, slices, _, _, q, lens, nq = _build(ob, w, dev, capacity=6400)
+        if ws is None:
+            ws = ob.alloc_workspace(1, 8, 32, 6400, device=dev)
+        out = torch.empty((1, 32, 128), dtype=torch.float32, device=dev)
+        ob.decode_attn(cache, torch.tensor(nq, dtype=torch.int32, device=dev),
+                       torch.tensor([lens[0] - nq[0]], dtype=torch.int32, device=dev), 6400,
+                       bits_to_dev_bf16(q, dev), SM, out, ws)
+        torch.cuda.synchronize()
+        assert_out_close(out.cpu().numpy(), _oracle_out(w, slices, q, lens), f"reuse {tag}")
+
+
 @pytest.mark.parametrize("case", ["cfg0", "cfg1", "ragged_g4", "g8"])
 def test_bf16_decode_matches_oracle(gpu_lib, case):
     from kv_cache_int2_fwht_amd import binding as ob

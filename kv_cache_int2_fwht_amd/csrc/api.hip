@@ -49,10 +49,11 @@ oscar_status launched(hipError_t e, const char* fn) {
   return ok();
 }
 
-// About two workgroups per compute unit: each wave then streams several
-// groups back to back (prefetching the next while computing the current).
+// About one 8-wave workgroup per compute unit: each wave then streams
+// several groups back to back (prefetching the next while computing the
+// current), and no younger workgroup waits behind an older one on a CU.
 #ifndef OSCAR_TARGET_BLOCKS
-#define OSCAR_TARGET_BLOCKS 512
+#define OSCAR_TARGET_BLOCKS 256
 #endif
 constexpr int64_t kTargetBlocks = OSCAR_TARGET_BLOCKS;
 constexpr int64_t kMinBlocks = OSCAR_TARGET_BLOCKS;

@@ -13,7 +13,7 @@
 
 namespace oscar {
 
-constexpr int kDecodeThreads = 256;
+constexpr int kDecodeThreads = 512;   // 8 waves: one workgroup fills a compute unit
 constexpr int kDecodeWaves = kDecodeThreads / kWave;
 constexpr float kLog2e = 1.4426950408889634f;
 

@@ -20,9 +20,10 @@
 // are recombined exactly and scaled back, so the only rounding is the 2^-26
 // relative fixed-point step of q' and p * vs.
 //
-// Work split: grid (split, KV head, sequence); 4 waves per workgroup; each
-// wave streams whole 128-token groups (prefetching the next group's bytes
-// while computing the current one) with a base-2 online softmax.  Lane
+// Work split: grid (split, KV head, sequence); one 8-wave workgroup per
+// compute unit; the waves claim the split's 128-token groups one at a time
+// (prefetching the next group's bytes while computing the current one) and
+// keep a base-2 online softmax each.  Lane
 // roles inside a wave (lane = 16 * r + n, w = n >> 1, u = 2 (n & 1)):
 //  * score / softmax lane (r, n): head r of the row block, the tokens
 //    16w + 4b + u + c of the group (b = 0..3, c = 0..1; column n of tile
@@ -155,6 +156,7 @@ struct Int2Smem {
   uint8_t a_qk[kDecodeWaves][Int2Cfg<G>::kRB][2 * 4 * kOpBlock];
   uint8_t a_pv[kDecodeWaves][Int2Cfg<G>::kRB][2 * 4 * kOpBlock];
   MergeSmem<G, Int2Cfg<G>::kSlots> merge;
+  int next_group;   // next group of this split not yet claimed by a wave
 };
 
 // Running softmax state of one wave: per row block, m (uniform over the
@@ -328,6 +330,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_int2_kernel(DecodeInt2A
   if (g < g_qend) load_group(buf0, a, slice, groups_cap, g, lane);
 
   if (wave == 0) clear_slot(sm.merge, kDecodeWaves);  // the tail slot stays empty unless a tail is seen
+  if (tid == 0) sm.next_group = g_begin + kDecodeWaves;   // published by the barriers below
   load_and_rotate_q<G, C::kRows>(a.q + (static_cast<size_t>(b) * a.num_q_heads + qh0) * kHeadDim,
                                  a.sm_scale * kLog2e, sm.q_raw, sm.u.q_rot);
 
@@ -353,16 +356,26 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_int2_kernel(DecodeInt2A
     for (int j = 0; j < 8; ++j) st.acc[rb][j] = 0.f;
   }
 
-  // two register buffers in turn: the next group streams in while the
-  // current one is computed
+  // Groups are handed out dynamically: each wave starts with group
+  // g_begin + wave and then claims the next unclaimed group of the split,
+  // so waves that get fewer issue slots simply process fewer groups.  Two
+  // register buffers in turn: the next group streams in while the current
+  // one is computed.
+  auto claim = [&]() -> int {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&sm.next_group, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
   while (g < g_qend) {
-    if (g + kDecodeWaves < g_qend) load_group(buf1, a, slice, groups_cap, g + kDecodeWaves, lane);
+    int g_next = claim();
+    if (g_next < g_qend) load_group(buf1, a, slice, groups_cap, g_next, lane);
     process_group<G>(buf0, g * kGroup, t_end, qv, fac, sm, st, wave, gl, n);
-    g += kDecodeWaves;
+    g = g_next;
     if (g >= g_qend) break;
-    if (g + kDecodeWaves < g_qend) load_group(buf0, a, slice, groups_cap, g + kDecodeWaves, lane);
+    g_next = claim();
+    if (g_next < g_qend) load_group(buf0, a, slice, groups_cap, g_next, lane);
     process_group<G>(buf1, g * kGroup, t_end, qv, fac, sm, st, wave, gl, n);
-    g += kDecodeWaves;
+    g = g_next;
   }
 
   // ---- this wave's state -> merge slot ----

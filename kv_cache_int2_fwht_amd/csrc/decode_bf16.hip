@@ -11,6 +11,9 @@
 namespace oscar {
 namespace {
 
+constexpr int kDecodeThreads = 512;   // 8 waves: one workgroup per compute unit
+constexpr int kDecodeWaves = kDecodeThreads / kWave;
+
 template <int G>
 struct Bf16Smem {
   float q_raw[G][kHeadDim];
@@ -39,8 +42,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeBf16A
   __shared__ Bf16Smem<G> sm;
 
   const int len = min(max(a.seq_len[b], 0), min(a.capacity, a.max_tokens));
-  const int t_begin = split * a.tokens_per_split;
-  const int t_end = min(t_begin + a.tokens_per_split, len);
+  // Split s owns the 128-token chunks s, s + S, s + 2S, ... (S = splits),
+  // so the workgroups of a head read neighbouring chunks at any moment.
+  const int S = a.splits;
+  const int t_end = len;
   const size_t slice = static_cast<size_t>(b) * a.num_kv_heads + h;
   const int qh0 = h * G;
   load_and_rotate_q<G, G>(a.q + (static_cast<size_t>(b) * a.num_q_heads + qh0) * kHeadDim, a.sm_scale * kLog2e,
@@ -54,15 +59,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeBf16A
     st.acc[hh][0] = st.acc[hh][1] = 0.f;
   }
 
-  const int c_begin = t_begin / kGroup;
-  const int c_end = (t_end + kGroup - 1) / kGroup;
-  for (int c = c_begin + wave; c < c_end; c += kDecodeWaves) {
+  const int c_end = (len + kGroup - 1) / kGroup;
+  for (int c = split + wave * S; c < c_end; c += kDecodeWaves * S) {
     const int t0 = c * kGroup;
     float logit[G][2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int t = t0 + lane + 64 * k;
-      const bool valid = t < t_end && t >= t_begin;
+      const bool valid = t < t_end;
       float dot[G];
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) dot[hh] = 0.f;

@@ -13,8 +13,6 @@
 
 namespace oscar {
 
-constexpr int kDecodeThreads = 512;   // 8 waves: one workgroup fills a compute unit
-constexpr int kDecodeWaves = kDecodeThreads / kWave;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // q [G][128] (bf16) -> dst_raw = q * scale and, if dst_rot is given,
@@ -24,7 +22,7 @@ template <int G, int kRows>
 __device__ void load_and_rotate_q(const uint16_t* q, float scale, float (*dst_raw)[kHeadDim],
                                   float (*dst_rot)[kHeadDim]) {
   const int tid = threadIdx.x;
-  for (int i = tid; i < kRows * kHeadDim; i += kDecodeThreads) {
+  for (int i = tid; i < kRows * kHeadDim; i += blockDim.x) {
     const float v = (i < G * kHeadDim) ? bf16_to_f32(q[i]) : 0.f;
     dst_raw[i / kHeadDim][i % kHeadDim] = v * scale;
     if (dst_rot) dst_rot[i / kHeadDim][i % kHeadDim] = v;
@@ -32,7 +30,7 @@ __device__ void load_and_rotate_q(const uint16_t* q, float scale, float (*dst_ra
   __syncthreads();
   if (!dst_rot) return;
   for (int bit = 1; bit < kHeadDim; bit <<= 1) {
-    for (int i = tid; i < G * kHeadDim / 2; i += kDecodeThreads) {
+    for (int i = tid; i < G * kHeadDim / 2; i += blockDim.x) {
       const int hh = i / (kHeadDim / 2);
       const int k = i % (kHeadDim / 2);
       // k enumerates the index pairs (lo, lo | bit) with lo's bit clear.
@@ -44,7 +42,7 @@ __device__ void load_and_rotate_q(const uint16_t* q, float scale, float (*dst_ra
     __syncthreads();
   }
   const float norm = scale * 0.088388347648318440550f;  // 1/sqrt(128)
-  for (int i = tid; i < G * kHeadDim; i += kDecodeThreads) dst_rot[i / kHeadDim][i % kHeadDim] *= norm;
+  for (int i = tid; i < G * kHeadDim; i += blockDim.x) dst_rot[i / kHeadDim][i % kHeadDim] *= norm;
   __syncthreads();
 }
 
@@ -79,7 +77,7 @@ __device__ void write_partial(MergeSmem<G, kSlots>& sm, float* partials, size_t 
                               int splits) {
   const int tid = threadIdx.x;
   __syncthreads();
-  for (int i = tid; i < G * kHeadDim; i += kDecodeThreads) {
+  for (int i = tid; i < G * kHeadDim; i += blockDim.x) {
     const int hh = i / kHeadDim;
     const int d = i % kHeadDim;
     float M = -INFINITY;

@@ -79,8 +79,10 @@ struct GroupBytes {
   uint2 ksz[4];     // (s | z << 16) of channels 16w + 4b + u + {0, 1}
 };
 
-__device__ __forceinline__ void load_group(GroupBytes& r, const DecodeInt2Args& a, size_t slice, int groups_cap,
-                                           int g, int lane) {
+// Bytes of group g needed by the score phase: key codes, norms, key scales
+// and zero-points, value scales and zero-points (used by the softmax).
+__device__ __forceinline__ void load_score_side(GroupBytes& r, const DecodeInt2Args& a, size_t slice, int groups_cap,
+                                                int g, int lane) {
   const int gl = lane >> 4;
   const int n = lane & 15;
   const int base = 16 * (n >> 1) + 2 * (n & 1);   // token / channel 16w + u
@@ -89,15 +91,23 @@ __device__ __forceinline__ void load_group(GroupBytes& r, const DecodeInt2Args& 
   const uint8_t* kc = a.k_codes + (row0 + base) * 32 + 8 * gl;
 #pragma unroll
   for (int i = 0; i < 8; ++i) r.kd[i] = *reinterpret_cast<const uint2*>(kc + (4 * (i & 3) + (i >> 2)) * 32);
-  const uint8_t* vc = a.v_codes + (grp * kHeadDim + n) * 32 + 8 * gl;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) r.vd[j] = *reinterpret_cast<const uint2*>(vc + j * 16 * 32);
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     r.nrm[b] = *reinterpret_cast<const uint32_t*>(a.k_norm + row0 + base + 4 * b);
     r.vsz[b] = *reinterpret_cast<const uint2*>(a.v_sz + (row0 + base + 4 * b) * 2);
     r.ksz[b] = *reinterpret_cast<const uint2*>(a.k_sz + (grp * kHeadDim + base + 4 * b) * 2);
   }
+}
+
+// Bytes of group g needed by the value phase: the value codes.
+__device__ __forceinline__ void load_value_side(GroupBytes& r, const DecodeInt2Args& a, size_t slice, int groups_cap,
+                                                int g, int lane) {
+  const int gl = lane >> 4;
+  const int n = lane & 15;
+  const size_t grp = slice * groups_cap + g;
+  const uint8_t* vc = a.v_codes + (grp * kHeadDim + n) * 32 + 8 * gl;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r.vd[j] = *reinterpret_cast<const uint2*>(vc + j * 16 * 32);
 }
 
 __device__ __forceinline__ uint32_t pick(const uint2& v, int c) { return c ? v.y : v.x; }
@@ -142,7 +152,11 @@ template <int G>
 struct Int2Cfg {
   static constexpr int kRB = (G + 3) / 4;  // 16-row blocks of (head, digit) rows
   static constexpr int kRows = kRB * 4;    // heads incl. zero padding
-  static constexpr int kSlots = kDecodeWaves + 1;  // waves + the bf16-tail state
+  // One workgroup per compute unit: 12 waves (3 per SIMD) while the kernel
+  // fits in 168 VGPRs, 8 waves for 8 query heads per KV head.
+  static constexpr int kWaves = (kRB == 1) ? 12 : 8;
+  static constexpr int kThreads = kWaves * kWave;
+  static constexpr int kSlots = kWaves + 1;  // waves + the bf16-tail state
 };
 
 template <int G>
@@ -153,8 +167,8 @@ struct Int2Smem {
     float tail_p[G][kGroup];                    // softmax weights of the bf16 tail tokens
   } u;
   // per wave and row block: MFMA A operands staged as [half][lane group][row][16 bytes]
-  uint8_t a_qk[kDecodeWaves][Int2Cfg<G>::kRB][2 * 4 * kOpBlock];
-  uint8_t a_pv[kDecodeWaves][Int2Cfg<G>::kRB][2 * 4 * kOpBlock];
+  uint8_t a_qk[Int2Cfg<G>::kWaves][Int2Cfg<G>::kRB][2 * 4 * kOpBlock];
+  uint8_t a_pv[Int2Cfg<G>::kWaves][Int2Cfg<G>::kRB][2 * 4 * kOpBlock];
   MergeSmem<G, Int2Cfg<G>::kSlots> merge;
   int next_group;   // next group of this split not yet claimed by a wave
 };
@@ -167,13 +181,14 @@ struct WaveRun {
   float m[RB], l[RB], z[RB], acc[RB][8];
 };
 
-// One quantized 128-token group: scores on the matrix cores, online softmax,
-// weighted value codes on the matrix cores.
+// Score phase of one quantized 128-token group: scores on the matrix cores,
+// online softmax update, p * vs staged as the value phase's A operand.
+// Returns the softmax rescale factors in alpha and inv_p.
 template <int G>
-__device__ __forceinline__ void process_group(const GroupBytes& cur, int t0, int t_end,
-                                              const float (&qv)[Int2Cfg<G>::kRB][2][4], const float (&fac)[2],
-                                              Int2Smem<G>& sm, WaveRun<Int2Cfg<G>::kRB>& st, int wave, int gl,
-                                              int n) {
+__device__ __forceinline__ void score_phase(const GroupBytes& cur, int t0, int t_end,
+                                            const float (&qv)[Int2Cfg<G>::kRB][2][4], const float (&fac)[2],
+                                            Int2Smem<G>& sm, WaveRun<Int2Cfg<G>::kRB>& st, int wave, int gl, int n,
+                                            float (&alpha)[Int2Cfg<G>::kRB], float (&inv_p)[Int2Cfg<G>::kRB]) {
   constexpr int RB = Int2Cfg<G>::kRB;
   const int tok_base = t0 + 16 * (n >> 1) + 2 * (n & 1);
   // ---- q' = Hq * s16 as 4-digit fixed point (A operand), Z = Hq . z16 ----
@@ -231,7 +246,6 @@ __device__ __forceinline__ void process_group(const GroupBytes& cur, int t0, int
   }
 
   // ---- online softmax (base 2) and p * vs as 4-digit fixed point ----
-  float inv_p[RB], alpha[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     float gm = logit[rb][0][0];
@@ -269,6 +283,15 @@ __device__ __forceinline__ void process_group(const GroupBytes& cur, int t0, int
         x[c][b] = balanced_digits(static_cast<int>(fmaf(pv[c][b], sc2 * fac[c], 0.5f)));
     stage_digits(sm.a_pv[wave][rb], x, gl, n);
   }
+}
+
+// Value phase: weighted value codes on the matrix cores (channel tile j,
+// column n = channel 16j + n), folded into the running accumulators.
+template <int G>
+__device__ __forceinline__ void value_phase(const GroupBytes& cur, Int2Smem<G>& sm, WaveRun<Int2Cfg<G>::kRB>& st,
+                                            int wave, int gl, int n, const float (&alpha)[Int2Cfg<G>::kRB],
+                                            const float (&inv_p)[Int2Cfg<G>::kRB]) {
+  constexpr int RB = Int2Cfg<G>::kRB;
   wave_sync_lds();
   v4i ap[RB][2];
 #pragma unroll
@@ -277,7 +300,6 @@ __device__ __forceinline__ void process_group(const GroupBytes& cur, int t0, int
     ap[rb][1] = read_operand(sm.a_pv[wave][rb], 1, gl, n);
   }
 
-  // ---- weighted value codes: channel tile j, column n = channel 16j + n ----
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const v4i b0 = spread_codes(cur.vd[j].x);
@@ -295,7 +317,7 @@ __device__ __forceinline__ void process_group(const GroupBytes& cur, int t0, int
 }
 
 template <int G>
-__global__ __launch_bounds__(kDecodeThreads) void decode_int2_kernel(DecodeInt2Args a) {
+__global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(DecodeInt2Args a) {
   using C = Int2Cfg<G>;
   constexpr int RB = C::kRB;
   const int split = blockIdx.x;
@@ -316,21 +338,25 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_int2_kernel(DecodeInt2A
   nt = min(max(nt, 0), kGroup - 1);
   if (a.k_tail == nullptr || a.v_tail == nullptr) nt = 0;
   const int total = min(nq + nt, a.max_tokens);
-  const int t_begin = split * a.tokens_per_split;
-  const int t_end = min(t_begin + a.tokens_per_split, total);
+  // Split s owns the groups s, s + S, s + 2S, ... (S = number of splits):
+  // at any moment the workgroups of a head read neighbouring groups, which
+  // spreads the traffic over all memory channels.
+  const int S = a.splits;
+  const int n_groups = (total + kGroup - 1) / kGroup;
   const size_t slice = static_cast<size_t>(b) * a.num_kv_heads + h;
   const int qh0 = h * G;
 
-  const int g_begin = t_begin / kGroup;
-  const int g_end = (t_end + kGroup - 1) / kGroup;
-  const int g_qend = min(g_end, nq / kGroup);   // quantized groups end here; a tail group may follow
-  int g = g_begin + wave;
+  const int g_qend = min(n_groups, nq / kGroup);   // quantized groups end here; a tail group may follow
+  int g = split + wave * S;
   // start streaming this wave's first group before the query set-up
-  GroupBytes buf0, buf1;
-  if (g < g_qend) load_group(buf0, a, slice, groups_cap, g, lane);
+  GroupBytes cur;
+  if (g < g_qend) {
+    load_score_side(cur, a, slice, groups_cap, g, lane);
+    load_value_side(cur, a, slice, groups_cap, g, lane);
+  }
 
-  if (wave == 0) clear_slot(sm.merge, kDecodeWaves);  // the tail slot stays empty unless a tail is seen
-  if (tid == 0) sm.next_group = g_begin + kDecodeWaves;   // published by the barriers below
+  if (wave == 0) clear_slot(sm.merge, C::kWaves);  // the tail slot stays empty unless a tail is seen
+  if (tid == 0) sm.next_group = C::kWaves;   // next group index k (group split + k S); published by the barriers below
   load_and_rotate_q<G, C::kRows>(a.q + (static_cast<size_t>(b) * a.num_q_heads + qh0) * kHeadDim,
                                  a.sm_scale * kLog2e, sm.q_raw, sm.u.q_rot);
 
@@ -356,25 +382,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_int2_kernel(DecodeInt2A
     for (int j = 0; j < 8; ++j) st.acc[rb][j] = 0.f;
   }
 
-  // Groups are handed out dynamically: each wave starts with group
-  // g_begin + wave and then claims the next unclaimed group of the split,
-  // so waves that get fewer issue slots simply process fewer groups.  Two
-  // register buffers in turn: the next group streams in while the current
-  // one is computed.
-  auto claim = [&]() -> int {
-    int v = 0;
-    if (lane == 0) v = atomicAdd(&sm.next_group, 1);
-    return __builtin_amdgcn_readfirstlane(v);
-  };
+  // Groups are handed out dynamically: each wave starts with the split's
+  // group number `wave` and then claims the next unclaimed one,
+  // so waves that get fewer issue slots simply process fewer groups.  One
+  // register set per wave: the next group's score-side bytes are requested
+  // as soon as the score phase has consumed the current ones, its value
+  // codes as soon as the value phase has.
   while (g < g_qend) {
-    int g_next = claim();
-    if (g_next < g_qend) load_group(buf1, a, slice, groups_cap, g_next, lane);
-    process_group<G>(buf0, g * kGroup, t_end, qv, fac, sm, st, wave, gl, n);
-    g = g_next;
-    if (g >= g_qend) break;
-    g_next = claim();
-    if (g_next < g_qend) load_group(buf0, a, slice, groups_cap, g_next, lane);
-    process_group<G>(buf1, g * kGroup, t_end, qv, fac, sm, st, wave, gl, n);
+    float alpha[RB], inv_p[RB];
+    score_phase<G>(cur, g * kGroup, total, qv, fac, sm, st, wave, gl, n, alpha, inv_p);
+    int k_next = 0;
+    if (lane == 0) k_next = atomicAdd(&sm.next_group, 1);
+    const int g_next = split + __builtin_amdgcn_readfirstlane(k_next) * S;
+    if (g_next < g_qend) load_score_side(cur, a, slice, groups_cap, g_next, lane);
+    value_phase<G>(cur, sm, st, wave, gl, n, alpha, inv_p);
+    if (g_next < g_qend) load_value_side(cur, a, slice, groups_cap, g_next, lane);
     g = g_next;
   }
 
@@ -396,10 +418,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_int2_kernel(DecodeInt2A
 
   // ---- the bf16 tail (at most one partial group, after the quantized ones) ----
   const int g_tail = nq / kGroup;
-  if (nt > 0 && g_tail >= g_begin && g_tail < g_end && wave == (g_tail - g_begin) % kDecodeWaves) {
-    const int n_tok = min(nt, t_end - g_tail * kGroup);
+  if (nt > 0 && g_tail < n_groups && g_tail % S == split && wave == (g_tail / S) % C::kWaves) {
+    const int n_tok = min(nt, total - g_tail * kGroup);
     bf16_tokens_wave<G, C::kSlots>(a.k_tail + slice * kGroup * kHeadDim, a.v_tail + slice * kGroup * kHeadDim,
-                                   n_tok, sm.q_raw, sm.u.tail_p, sm.merge, kDecodeWaves);
+                                   n_tok, sm.q_raw, sm.u.tail_p, sm.merge, C::kWaves);
   }
 
   const size_t partial_base = (static_cast<size_t>(b) * a.num_q_heads + qh0) * a.splits;
@@ -409,7 +431,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_int2_kernel(DecodeInt2A
 template <int G>
 hipError_t launch_g(const DecodeInt2Args& a, int32_t batch, hipStream_t s) {
   dim3 grid(a.splits, a.num_kv_heads, batch);
-  hipLaunchKernelGGL(decode_int2_kernel<G>, grid, dim3(kDecodeThreads), 0, s, a);
+  hipLaunchKernelGGL(decode_int2_kernel<G>, grid, dim3(Int2Cfg<G>::kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -17,24 +17,26 @@ namespace oscar {
 namespace {
 
 constexpr int kMergeUnroll = 8;
+constexpr int kMergeThreads = 256;
+constexpr int kMergeWaves = kMergeThreads / kWave;
 
-__global__ __launch_bounds__(kDecodeThreads) void merge_splits_kernel(const float* __restrict__ partials,
+__global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(const float* __restrict__ partials,
                                                                        float* __restrict__ out, int num_q_heads,
                                                                        int splits) {
   const int qh = blockIdx.x;
   const int b = blockIdx.y;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  __shared__ float sm_m[kDecodeWaves], sm_l[kDecodeWaves];
-  __shared__ float2 sm_acc[kDecodeWaves][kWave];
+  __shared__ float sm_m[kMergeWaves], sm_l[kMergeWaves];
+  __shared__ float2 sm_acc[kMergeWaves][kWave];
   const float* base = partials + (static_cast<size_t>(b) * num_q_heads + qh) * splits * kPartialFloats;
 
   float M = -INFINITY, L = 0.f, a0 = 0.f, a1 = 0.f;
-  for (int s0 = wave; s0 < splits; s0 += kDecodeWaves * kMergeUnroll) {
+  for (int s0 = wave; s0 < splits; s0 += kMergeWaves * kMergeUnroll) {
     float2 ml[kMergeUnroll], v[kMergeUnroll];
 #pragma unroll
     for (int k = 0; k < kMergeUnroll; ++k) {   // all loads of the batch first
-      const int s = s0 + k * kDecodeWaves;
+      const int s = s0 + k * kMergeWaves;
       if (s < splits) {
         const float* rec = base + static_cast<size_t>(s) * kPartialFloats;
         ml[k] = *reinterpret_cast<const float2*>(rec);
@@ -66,11 +68,11 @@ __global__ __launch_bounds__(kDecodeThreads) void merge_splits_kernel(const floa
   if (wave == 0) {
     float Mt = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) Mt = fmaxf(Mt, sm_m[w]);
+    for (int w = 0; w < kMergeWaves; ++w) Mt = fmaxf(Mt, sm_m[w]);
     float Lt = 0.f, r0 = 0.f, r1 = 0.f;
     if (Mt != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) {
+      for (int w = 0; w < kMergeWaves; ++w) {
         if (sm_m[w] == -INFINITY) continue;
         const float f = exp2f(sm_m[w] - Mt);
         Lt = fmaf(sm_l[w], f, Lt);
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(kDecodeThreads) void merge_splits_kernel(const floa
 hipError_t launch_merge(const float* partials, float* out, int32_t batch, int32_t num_kv_heads, int32_t num_q_heads,
                         int32_t splits, hipStream_t s) {
   (void)num_kv_heads;
-  hipLaunchKernelGGL(merge_splits_kernel, dim3(num_q_heads, batch), dim3(kDecodeThreads), 0, s, partials, out,
+  hipLaunchKernelGGL(merge_splits_kernel, dim3(num_q_heads, batch), dim3(kMergeThreads), 0, s, partials, out,
                      num_q_heads, splits);
   return hipGetLastError();
 }

@@ -176,6 +176,42 @@ oscar_status oscar_decode_attn(const oscar_kv_cache* cache,
                                void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The two halves of oscar_decode_attn, for callers that combine partial
+ * softmax states themselves (for instance a sequence split across devices:
+ * each device scores its own tokens, the records are gathered along the
+ * split axis and merged once).
+ *
+ * oscar_decode_num_splits -- records per (sequence, query head) that
+ * oscar_decode_attn_splits writes for this shape (0 for invalid shapes).
+ *
+ * oscar_decode_attn_splits -- the first kernel of oscar_decode_attn: same
+ * arguments except out.  It writes, at the start of ws, the float records
+ * [batch][num_q_heads][S][132] (S = oscar_decode_num_splits(batch,
+ * num_kv_heads, max_tokens)); record (b, j, r) = (m, l, unused, unused,
+ * acc[128]) over the tokens of split r of sequence b, in base 2:
+ * m = max_t x_t with x_t = logit_t * log2(e) (-inf if the split saw no
+ * token), l = sum_t 2^(x_t - m), acc[d] = sum_t 2^(x_t - m) * value_t[d]
+ * (l = acc = 0 for an empty split).
+ *
+ * oscar_decode_merge -- out[b][j] = sum_r w_r acc_r / sum_r w_r l_r with
+ * w_r = 2^(m_r - max_r m_r), over the num_splits records of (b, j) stored
+ * as above at partials; records with m = -inf are skipped and out = 0 if
+ * all are.  Records are combined in a fixed order (deterministic).
+ * partials, out: device memory, 16-byte aligned; batch <= 65535.
+ */
+int32_t oscar_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_tokens);
+
+oscar_status oscar_decode_attn_splits(const oscar_kv_cache* cache,
+                                      const int32_t* n_quant, const int32_t* n_tail,
+                                      int32_t max_tokens, const uint16_t* q,
+                                      int32_t num_q_heads, float sm_scale,
+                                      void* ws, size_t ws_bytes, void* stream);
+
+oscar_status oscar_decode_merge(const float* partials, int32_t batch,
+                                int32_t num_q_heads, int32_t num_splits,
+                                float* out, void* stream);
+
+/*
  * oscar_decode_attn_bf16 -- the same decode step over unquantized bf16
  * keys and values: plain split-K flash-decoding, the counterpart of the
  * BF16 FlashDecoding-v2 baseline the pages compare against.

@@ -51,6 +51,7 @@ EXPORTED = (
     "oscar_abi_version", "oscar_status_string", "oscar_last_error",
     "oscar_quantize_kv", "oscar_decode_workspace_bytes",
     "oscar_decode_attn", "oscar_decode_attn_bf16",
+    "oscar_decode_num_splits", "oscar_decode_attn_splits", "oscar_decode_merge",
 )
 
 
@@ -82,6 +83,12 @@ def lib():
     L.oscar_decode_attn.argtypes = [ctypes.POINTER(KVCacheDesc), vp, vp, i32, vp, i32, f32, vp, vp, sz, vp]
     L.oscar_decode_attn_bf16.restype = ctypes.c_int
     L.oscar_decode_attn_bf16.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz, vp]
+    L.oscar_decode_num_splits.restype = i32
+    L.oscar_decode_num_splits.argtypes = [i32, i32, i32]
+    L.oscar_decode_attn_splits.restype = ctypes.c_int
+    L.oscar_decode_attn_splits.argtypes = [ctypes.POINTER(KVCacheDesc), vp, vp, i32, vp, i32, f32, vp, sz, vp]
+    L.oscar_decode_merge.restype = ctypes.c_int
+    L.oscar_decode_merge.argtypes = [vp, i32, i32, i32, vp, vp]
     _lib = L
     return L
 
@@ -224,3 +231,42 @@ def decode_attn_bf16(k: torch.Tensor, v: torch.Tensor, seq_len: torch.Tensor, ma
                                         _ptr(q, torch.bfloat16, "q"), q.shape[1], float(sm_scale),
                                         _ptr(out, torch.float32, "out"), _ptr(ws, torch.uint8, "ws"),
                                         ws.numel(), _stream(stream)))
+
+
+def decode_num_splits(batch: int, num_kv_heads: int, max_tokens: int) -> int:
+    """oscar_decode_num_splits: records per (sequence, query head)."""
+    return int(lib().oscar_decode_num_splits(batch, num_kv_heads, max_tokens))
+
+
+def decode_attn_splits(cache: PackedCache, n_quant: torch.Tensor, n_tail: torch.Tensor, max_tokens: int,
+                       q: torch.Tensor, sm_scale: float, ws: torch.Tensor,
+                       stream: Optional[torch.cuda.Stream] = None) -> None:
+    """oscar_decode_attn_splits: the split records of one decode step,
+    written at the start of ws as float [B, Hq, S, 132]."""
+    if q.dim() != 3 or q.shape[0] != cache.batch or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [batch, q_heads, 128]")
+    d = cache.desc()
+    _check(lib().oscar_decode_attn_splits(ctypes.byref(d), _ptr(n_quant, torch.int32, "n_quant"),
+                                          _ptr(n_tail, torch.int32, "n_tail"), int(max_tokens),
+                                          _ptr(q, torch.bfloat16, "q"), q.shape[1], float(sm_scale),
+                                          _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+
+
+def split_records(ws: torch.Tensor, batch: int, num_q_heads: int, num_splits: int) -> torch.Tensor:
+    """View of the records at the start of a workspace: float [B, Hq, S, 132]."""
+    n = batch * num_q_heads * num_splits * 132
+    if ws.dtype != torch.uint8 or ws.numel() < 4 * n:
+        raise ValueError("workspace too small for these records")
+    return ws[:4 * n].view(torch.float32).view(batch, num_q_heads, num_splits, 132)
+
+
+def decode_merge(partials: torch.Tensor, out: torch.Tensor,
+                 stream: Optional[torch.cuda.Stream] = None) -> None:
+    """oscar_decode_merge.  partials float [B, Hq, S, 132]; out fp32 [B, Hq, 128]."""
+    if partials.dim() != 4 or partials.shape[3] != 132:
+        raise ValueError("partials must be [batch, q_heads, splits, 132]")
+    B, Hq, S, _ = partials.shape
+    if out.shape != (B, Hq, HEAD_DIM):
+        raise ValueError("out must be [batch, q_heads, 128]")
+    _check(lib().oscar_decode_merge(_ptr(partials, torch.float32, "partials"), B, Hq, S,
+                                    _ptr(out, torch.float32, "out"), _stream(stream)))

@@ -188,15 +188,21 @@ size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t
   return partial_bytes(batch, num_q_heads, splits);
 }
 
-oscar_status oscar_decode_attn(const oscar_kv_cache* cache, const int32_t* n_quant, const int32_t* n_tail,
-                               int32_t max_tokens, const uint16_t* q, int32_t num_q_heads, float sm_scale,
-                               float* out, void* ws, size_t ws_bytes, void* stream) {
-  const char* fn = "oscar_decode_attn";
+}  // extern "C"
+
+namespace {
+
+// Validation and launch of the INT2 decode kernel (the split records); out
+// is checked only when the caller also merges.
+oscar_status decode_int2_splits(const char* fn, const oscar_kv_cache* cache, const int32_t* n_quant,
+                                const int32_t* n_tail, int32_t max_tokens, const uint16_t* q, int32_t num_q_heads,
+                                float sm_scale, const float* out, bool with_out, void* ws, size_t ws_bytes,
+                                hipStream_t s, int32_t* splits_out) {
   oscar_status st = check_cache(fn, cache);
   if (st != OSCAR_OK) return st;
   if ((st = check_heads(fn, cache->batch, cache->num_kv_heads, num_q_heads)) != OSCAR_OK) return st;
-  if (!n_quant || !n_tail || !q || !out || !ws) return fail(OSCAR_EINVAL, "%s: NULL argument", fn);
-  if (!aligned16(q) || !aligned16(out) || !aligned16(ws))
+  if (!n_quant || !n_tail || !q || !ws || (with_out && !out)) return fail(OSCAR_EINVAL, "%s: NULL argument", fn);
+  if (!aligned16(q) || !aligned16(ws) || (with_out && !aligned16(out)))
     return fail(OSCAR_EINVAL, "%s: q, out and ws must be 16-byte aligned", fn);
   if (max_tokens < 0) return fail(OSCAR_EINVAL, "%s: max_tokens must be >= 0", fn);
   if (max_tokens > cache->capacity + OSCAR_GROUP - 1)
@@ -224,9 +230,51 @@ oscar_status oscar_decode_attn(const oscar_kv_cache* cache, const int32_t* n_qua
   a.tokens_per_split = p.tokens_per_split;
   a.splits = p.splits;
   a.sm_scale = sm_scale;
+  *splits_out = p.splits;
+  return launched(launch_decode_int2(a, cache->batch, s), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t oscar_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_tokens) {
+  if (batch <= 0 || num_kv_heads <= 0 || max_tokens < 0) return 0;
+  return plan_int2(batch, num_kv_heads, max_tokens).splits;
+}
+
+oscar_status oscar_decode_attn_splits(const oscar_kv_cache* cache, const int32_t* n_quant, const int32_t* n_tail,
+                                      int32_t max_tokens, const uint16_t* q, int32_t num_q_heads, float sm_scale,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  int32_t splits = 0;
+  return decode_int2_splits("oscar_decode_attn_splits", cache, n_quant, n_tail, max_tokens, q, num_q_heads,
+                            sm_scale, nullptr, false, ws, ws_bytes, static_cast<hipStream_t>(stream), &splits);
+}
+
+oscar_status oscar_decode_merge(const float* partials, int32_t batch, int32_t num_q_heads, int32_t num_splits,
+                                float* out, void* stream) {
+  const char* fn = "oscar_decode_merge";
+  if (!partials || !out) return fail(OSCAR_EINVAL, "%s: NULL argument", fn);
+  if (!aligned16(partials) || !aligned16(out))
+    return fail(OSCAR_EINVAL, "%s: partials and out must be 16-byte aligned", fn);
+  if (batch <= 0 || batch > 65535 || num_q_heads <= 0 || num_splits <= 0)
+    return fail(OSCAR_EINVAL, "%s: batch must be in [1, 65535], num_q_heads and num_splits positive", fn);
+  oscar_status st = check_device(fn);
+  if (st != OSCAR_OK) return st;
+  return launched(launch_merge(partials, out, batch, num_q_heads, num_splits, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+oscar_status oscar_decode_attn(const oscar_kv_cache* cache, const int32_t* n_quant, const int32_t* n_tail,
+                               int32_t max_tokens, const uint16_t* q, int32_t num_q_heads, float sm_scale,
+                               float* out, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "oscar_decode_attn";
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = launched(launch_decode_int2(a, cache->batch, s), fn)) != OSCAR_OK) return st;
-  return launched(launch_merge(a.partials, out, cache->batch, cache->num_kv_heads, num_q_heads, p.splits, s), fn);
+  int32_t splits = 0;
+  oscar_status st = decode_int2_splits(fn, cache, n_quant, n_tail, max_tokens, q, num_q_heads, sm_scale, out, true,
+                                       ws, ws_bytes, s, &splits);
+  if (st != OSCAR_OK) return st;
+  return launched(launch_merge(static_cast<const float*>(ws), out, cache->batch, num_q_heads, splits, s), fn);
 }
 
 oscar_status oscar_decode_attn_bf16(const uint16_t* k, const uint16_t* v, int32_t batch, int32_t num_kv_heads,
@@ -261,7 +309,7 @@ oscar_status oscar_decode_attn_bf16(const uint16_t* k, const uint16_t* v, int32_
   a.sm_scale = sm_scale;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = launched(launch_decode_bf16(a, batch, s), fn)) != OSCAR_OK) return st;
-  return launched(launch_merge(a.partials, out, batch, num_kv_heads, num_q_heads, p.splits, s), fn);
+  return launched(launch_merge(a.partials, out, batch, num_q_heads, p.splits, s), fn);
 }
 
 }  // extern "C"

@@ -81,7 +81,7 @@ struct DecodeBf16Args {
 hipError_t launch_quantize(const QuantizeArgs& a, int32_t batch, int32_t max_groups, hipStream_t s);
 hipError_t launch_decode_int2(const DecodeInt2Args& a, int32_t batch, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeBf16Args& a, int32_t batch, hipStream_t s);
-hipError_t launch_merge(const float* partials, float* out, int32_t batch, int32_t num_kv_heads,
-                        int32_t num_q_heads, int32_t splits, hipStream_t s);
+hipError_t launch_merge(const float* partials, float* out, int32_t batch, int32_t num_q_heads, int32_t splits,
+                        hipStream_t s);
 
 }  // namespace oscar

@@ -87,9 +87,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(const float
 
 }  // namespace
 
-hipError_t launch_merge(const float* partials, float* out, int32_t batch, int32_t num_kv_heads, int32_t num_q_heads,
-                        int32_t splits, hipStream_t s) {
-  (void)num_kv_heads;
+hipError_t launch_merge(const float* partials, float* out, int32_t batch, int32_t num_q_heads, int32_t splits,
+                        hipStream_t s) {
   hipLaunchKernelGGL(merge_splits_kernel, dim3(num_q_heads, batch), dim3(kMergeThreads), 0, s, partials, out,
                      num_q_heads, splits);
   return hipGetLastError();

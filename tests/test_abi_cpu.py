@@ -51,6 +51,12 @@ def test_workspace_size_rules():
     assert f(1, 8, 32, 0) > 0              # an empty cache still gets one (empty) split
     # one 528-byte partial record per (sequence, query head, split) at least
     assert f(8, 8, 32, 131072) >= 8 * 32 * 528
+    for B, H, Hq, T in [(1, 8, 32, 131072), (8, 8, 32, 131072), (1, 1, 4, 1024), (3, 2, 16, 5000)]:
+        S = ob.decode_num_splits(B, H, T)
+        assert S >= 1
+        assert f(B, H, Hq, T) >= B * Hq * S * 528
+    assert ob.decode_num_splits(0, 8, 1024) == 0
+    assert ob.decode_num_splits(1, 8, -1) == 0
 
 
 def _no_gpu():
@@ -98,6 +104,30 @@ def test_decode_validation_errors():
 def test_valid_call_without_device_reports_hip_error():
     assert _decode(_desc()) == ob.OSCAR_EHIP
     assert b"no HIP device" in ob.lib().oscar_last_error()
+
+
+@needs_no_gpu
+def test_splits_and_merge_validation_errors():
+    L = ob.lib()
+
+    def sp(desc, ws=0xA0000, ws_bytes=1 << 26, q=0x80000):
+        return L.oscar_decode_attn_splits(ctypes.byref(desc), 0x100, 0x200, 1024, q, 32, 0.088, ws, ws_bytes, None)
+
+    assert sp(_desc(), ws=0) == ob.OSCAR_EINVAL
+    assert sp(_desc(), q=0x80002) == ob.OSCAR_EINVAL
+    assert sp(_desc(), ws_bytes=100) == ob.OSCAR_EWORKSPACE
+    assert sp(_desc(head_dim=96)) == ob.OSCAR_EUNSUPPORTED
+    assert sp(_desc()) == ob.OSCAR_EHIP
+
+    def mg(p=0x10000, B=1, Hq=32, S=4, out=0x20000):
+        return L.oscar_decode_merge(p, B, Hq, S, out, None)
+
+    assert mg(p=0) == ob.OSCAR_EINVAL
+    assert mg(out=0x20008) == ob.OSCAR_EINVAL
+    assert mg(B=0) == ob.OSCAR_EINVAL
+    assert mg(B=65536) == ob.OSCAR_EINVAL
+    assert mg(S=0) == ob.OSCAR_EINVAL
+    assert mg() == ob.OSCAR_EHIP
 
 
 @needs_no_gpu

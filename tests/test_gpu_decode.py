@@ -125,6 +125,42 @@ def test_int2_decode_reused_workspace_sees_fresh_partials(gpu_lib):
         assert_out_close(out.cpu().numpy(), _oracle_out(w, slices, q, lens), f"reuse {tag}")
 
 
+def test_workspace_shared_across_shapes_and_kernels(gpu_lib):
+    """One workspace for calls of different shapes, INT2 and bf16 in turn:
+    each call, whatever its (batch, KV heads) and split count, must merge
+    exactly the partial records it wrote itself."""
+    from kv_cache_int2_fwht_amd import binding as ob
+    dev = torch.device("cuda:0")
+    shapes = [(1, 8, 2, [9000], 113), (3, 64, 8, [700, 2500, 129], 114), (1, 2, 1, [40], 115),
+              (2, 16, 4, [5000, 1], 116), (3, 8, 8, [300, 0, 8000], 117)]
+    n = max(ob.decode_workspace_bytes(B, hkv, hq, max(lens)) for B, hq, hkv, lens, _ in shapes)
+    ws = torch.zeros(n, dtype=torch.uint8, device=dev)
+    for B, hq, hkv, lens, tag in shapes:
+        w = syn.custom_workload(B, hq, hkv, lens, cfg_tag=tag)
+        _say(f"shared workspace: B={B} Hq={hq} Hkv={hkv} lens={lens}")
+        cache, slices, kraw, vraw, q, lens_, nq = _build(ob, w, dev)
+        mt = max(lens_)
+        out = torch.full((B, hq, 128), float("nan"), dtype=torch.float32, device=dev)
+        ob.decode_attn(cache, torch.tensor(nq, dtype=torch.int32, device=dev),
+                       torch.tensor([n - m for n, m in zip(lens_, nq)], dtype=torch.int32, device=dev),
+                       mt, bits_to_dev_bf16(q, dev), SM, out, ws)
+        torch.cuda.synchronize()
+        assert_out_close(out.cpu().numpy(), _oracle_out(w, slices, q, lens_), f"int2 {tag}")
+        out_bf = torch.full((B, hq, 128), float("nan"), dtype=torch.float32, device=dev)
+        ob.decode_attn_bf16(bits_to_dev_bf16(kraw, dev), bits_to_dev_bf16(vraw, dev),
+                            torch.tensor(lens_, dtype=torch.int32, device=dev), mt,
+                            bits_to_dev_bf16(q, dev), SM, out_bf, ws)
+        torch.cuda.synchronize()
+        G = hq // hkv
+        ref = np.zeros((B, hq, 128))
+        for b in range(B):
+            for h in range(hkv):
+                ref[b, h * G:(h + 1) * G] = oracle.decode_bf16_slice(
+                    syn.bf16_bits_to_f64(q[b, h * G:(h + 1) * G]), syn.bf16_bits_to_f64(kraw[b, h, :lens_[b]]),
+                    syn.bf16_bits_to_f64(vraw[b, h, :lens_[b]]), SM)
+        assert_out_close(out_bf.cpu().numpy(), ref, f"bf16 {tag}")
+
+
 @pytest.mark.parametrize("case", ["cfg0", "cfg1", "ragged_g4", "g8"])
 def test_bf16_decode_matches_oracle(gpu_lib, case):
     from kv_cache_int2_fwht_amd import binding as ob
@@ -168,3 +204,70 @@ def test_workspace_too_small_is_an_error(gpu_lib):
     with pytest.raises(ob.OscarError) as e:
         ob.decode_attn(cache, z, z, 1024, q, SM, out, ws)
     assert e.value.status == ob.OSCAR_EWORKSPACE
+
+
+def test_splits_then_merge_equals_decode(gpu_lib):
+    """oscar_decode_attn_splits + oscar_decode_merge give oscar_decode_attn's
+    output bit for bit, and the records are softmax states whose merge (by
+    the oracle's algebra, in float64) is the oracle's attention output."""
+    from kv_cache_int2_fwht_amd import binding as ob
+    dev = torch.device("cuda:0")
+    w = syn.custom_workload(2, 16, 4, [2500, 700 + 45], cfg_tag=118)
+    cache, slices, _, _, q, lens, nq = _build(ob, w, dev)
+    mt = max(lens)
+    full, ws = _run_int2(ob, cache, q, lens, nq, dev)
+    S = ob.decode_num_splits(w.batch, w.num_kv_heads, mt)
+    assert S >= 1
+    ob.decode_attn_splits(cache, torch.tensor(nq, dtype=torch.int32, device=dev),
+                          torch.tensor([n - m for n, m in zip(lens, nq)], dtype=torch.int32, device=dev),
+                          mt, bits_to_dev_bf16(q, dev), SM, ws)
+    rec = ob.split_records(ws, w.batch, w.num_q_heads, S)
+    out = torch.full((w.batch, w.num_q_heads, 128), float("nan"), dtype=torch.float32, device=dev)
+    ob.decode_merge(rec, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), full)
+    r = rec.cpu().numpy().astype(np.float64)
+    ref = _oracle_out(w, slices, q, lens)
+    ln2 = np.log(2.0)
+    for b in range(w.batch):
+        for j in range(w.num_q_heads):
+            states = [(r[b, j, s, 0] * ln2, r[b, j, s, 1], r[b, j, s, 4:]) for s in range(S)]
+            got = oracle.merge_states(states)
+            assert_out_close(got[None, None], ref[b:b + 1, j:j + 1], f"records b={b} head={j}")
+
+
+def test_merge_of_records_from_two_token_shards(gpu_lib):
+    """A sequence held as two caches (tokens [0, 1024) and [1024, n), the
+    second with the bf16 tail): the records of both, concatenated along the
+    split axis and merged once, give attention over the whole sequence."""
+    from kv_cache_int2_fwht_amd import binding as ob
+    dev = torch.device("cuda:0")
+    n = 3000 + 37
+    w = syn.custom_workload(1, 8, 2, [n], cfg_tag=119)
+    B, H, Hq = 1, 2, 8
+    n_q_full = syn.split_lengths(n)[0]
+    parts = [(0, 1024), (1024, n)]
+    recs = []
+    full_slices = {}
+    qd = bits_to_dev_bf16(np.stack([syn.query(w, 0)]), dev)
+    for lo, hi in parts:
+        m = hi - lo
+        nq = syn.split_lengths(m)[0]
+        cache = ob.PackedCache(B, H, max(128, ((m + 127) // 128) * 128), device=dev)
+        for h in range(H):
+            kb = syn.bf16_bits_to_f64(syn.keys_slice(w, 0, h))
+            vb = syn.bf16_bits_to_f64(syn.values_slice(w, 0, h))
+            upload_slice(cache, 0, h, oracle.quantize_slice(kb[lo:hi], vb[lo:hi], nq))
+            if (lo, hi) == parts[0]:
+                full_slices[0, h] = oracle.quantize_slice(kb, vb, n_q_full)
+        ws = ob.alloc_workspace(B, H, Hq, m, device=dev)
+        ob.decode_attn_splits(cache, torch.tensor([nq], dtype=torch.int32, device=dev),
+                              torch.tensor([m - nq], dtype=torch.int32, device=dev), m, qd, SM, ws)
+        S = ob.decode_num_splits(B, H, m)
+        recs.append(ob.split_records(ws, B, Hq, S).clone())
+    allrec = torch.cat(recs, dim=2).contiguous()
+    out = torch.full((B, Hq, 128), float("nan"), dtype=torch.float32, device=dev)
+    ob.decode_merge(allrec, out)
+    torch.cuda.synchronize()
+    q = np.stack([syn.query(w, 0)])
+    assert_out_close(out.cpu().numpy(), _oracle_out(w, full_slices, q, [n]), "two shards")

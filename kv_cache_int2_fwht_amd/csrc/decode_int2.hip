@@ -42,26 +42,76 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// 16 / (weight of a code at bit position 2r of its byte after the spread):
-// r = 0 -> mask 0x03 (weight 1), r = 1 -> 0x0C (4), r = 2 -> 0x30 (16),
-// r = 3 -> shifted down by 6 (weight 1).
-__device__ constexpr float kInvWeight16[4] = {16.f, 4.f, 1.f, 16.f};
+// After the spread (spread_codes) the code at bit position 2r of its byte
+// carries the weight 4^r (masks 0x03, 0x0C, 0x30, 0xC0); the other operand
+// is multiplied by 64 / 4^r so that every code ends up with weight 64.
+__device__ constexpr float kFac[4] = {64.f, 16.f, 4.f, 1.f};
 
 // 16 packed codes (bits 2k..2k+1 = code k) -> 16 int8 lanes of an MFMA
-// operand.  Byte b of output dword r holds code 4b + r times its weight.
+// operand.  Byte b of output dword r holds code 4b + r times 4^r; the top
+// field is flipped into int8 range, 64 * code - 128, and the -128 is
+// cancelled by the accumulator's start value (field3_bias).
 __device__ __forceinline__ v4i spread_codes(uint32_t x) {
   v4i o;
   o[0] = static_cast<int>(x & 0x03030303u);
   o[1] = static_cast<int>(x & 0x0C0C0C0Cu);
   o[2] = static_cast<int>(x & 0x30303030u);
-  o[3] = static_cast<int>((x >> 6) & 0x03030303u);
+  o[3] = static_cast<int>((x & 0xC0C0C0C0u) ^ 0x80808080u);
   return o;
 }
 
-// Four signed base-256 digits of |v| < 2^31 - 2^24: digit k is byte k of the
-// result read as int8 (balanced representation).
-__device__ __forceinline__ uint32_t balanced_digits(int v) {
-  return static_cast<uint32_t>(v + 0x808080) ^ 0x808080u;
+// 128 * (sum of the A operand over the K positions that carry top-field
+// codes), the start value that cancels the -128 offset of spread_codes in a
+// two-step (K = 128) product with A halves a0, a1.
+__device__ __forceinline__ v4i field3_bias(const v4i& a0, const v4i& a1) {
+  const v4i b64 = {0, 0, 0, 0x40404040};   // 64 at the top-field positions
+  v4i c = {0, 0, 0, 0};
+  c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b64, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b64, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b64, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b64, c, 0, 0, 0);
+  return c;
+}
+
+// Four signed base-256 digits of an integer v, |v| < 2^31 - 2^24, given as
+// v_off = v + 0x808080: digit k is byte k of the result read as int8
+// (balanced representation).
+__device__ __forceinline__ uint32_t balanced_digits_off(int v_off) {
+  return static_cast<uint32_t>(v_off) ^ 0x808080u;
+}
+
+// An integer within one unit of y (|y| < 2^30), plus 0x808080, for
+// balanced_digits_off.  The offset and the rounding half are added in fp32
+// and the sum is truncated: round half up wherever the sum is positive.
+__device__ __forceinline__ int fixed_off(float y) { return static_cast<int>(y + 8421504.5f); }
+
+// 2^x for x <= 0 with the hardware exponential: results below 2^-126 flush
+// to zero (negligible weights in a softmax); 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Maximum over the 16 lanes of a DPP row of non-negative floats (compared as
+// their bit patterns, which order them).
+__device__ __forceinline__ float row_max16_nonneg(float x) {
+  int v = __float_as_int(x);
+  v = max(v, __builtin_amdgcn_mov_dpp(v, kDppQuadXor1, 0xF, 0xF, true));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, kDppQuadXor2, 0xF, 0xF, true));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, kDppRowRor4, 0xF, 0xF, true));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, kDppRowRor8, 0xF, 0xF, true));
+  return __int_as_float(v);
+}
+
+// Maximum over the 16 lanes of a DPP row of floats that are not NaN: each
+// float is mapped to an int with the same order (negative values have their
+// magnitude bits flipped), reduced, and mapped back (the map is its own
+// inverse).
+__device__ __forceinline__ int float_order_key(int bits) { return bits ^ ((bits >> 31) & 0x7FFFFFFF); }
+__device__ __forceinline__ float row_max16_ordered(float x) {
+  int v = float_order_key(__float_as_int(x));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, kDppQuadXor1, 0xF, 0xF, true));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, kDppQuadXor2, 0xF, 0xF, true));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, kDppRowRor4, 0xF, 0xF, true));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, kDppRowRor8, 0xF, 0xF, true));
+  return __int_as_float(float_order_key(v));
 }
 
 // Recombine the four digit rows of one (head, column) of an MFMA result.
@@ -202,29 +252,30 @@ __device__ __forceinline__ void score_phase(const GroupBytes& cur, int t0, int t
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const uint32_t w = pick(cur.ksz[b], c);
-        qs[c][b] = qv[rb][c][b] * f16_lo(w);
+        qs[c][b] = fmaf(qv[rb][c][b], f16_lo(w), 0.f);   // one mixed-precision FMA
         zp = fmaf(qv[rb][c][b], f16_hi(w), zp);
         amax = fmaxf(amax, fabsf(qs[c][b]));
       }
-    amax = row_max16(amax);
+    amax = row_max16_nonneg(amax);
     Zg[rb] = row_sum16(zp);
     int e;
     frexpf(amax, &e);                        // amax < 2^e
-    const float sc = ldexpf(1.f, 26 - e);    // |q' * sc| < 2^26
-    inv_q[rb] = ldexpf(1.f, e - 30);         // 1 / (sc * 16)
+    const float sc = ldexpf(1.f, 24 - e);    // |q' * sc| < 2^24, |q' * sc * fac| < 2^30
+    inv_q[rb] = ldexpf(1.f, e - 30);         // 1 / (sc * 64)
     uint32_t x[2][4];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) x[c][b] = balanced_digits(static_cast<int>(rintf(qs[c][b] * (sc * fac[c]))));
+      for (int b = 0; b < 4; ++b) x[c][b] = balanced_digits_off(fixed_off(qs[c][b] * (sc * fac[c])));
     stage_digits(sm.a_qk[wave][rb], x, gl, n);
   }
   wave_sync_lds();
-  v4i aq[RB][2];
+  v4i aq[RB][2], bias[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     aq[rb][0] = read_operand(sm.a_qk[wave][rb], 0, gl, n);
     aq[rb][1] = read_operand(sm.a_qk[wave][rb], 1, gl, n);
+    bias[rb] = field3_bias(aq[rb][0], aq[rb][1]);
   }
 
   // ---- scores: column n of tile i = 4c + b is token 16w + 4b + u + c ----
@@ -235,13 +286,20 @@ __device__ __forceinline__ void score_phase(const GroupBytes& cur, int t0, int t
     const v4i b0 = spread_codes(cur.kd[i].x);
     const v4i b1 = spread_codes(cur.kd[i].y);
     const float n16 = c ? f16_hi(cur.nrm[b]) : f16_lo(cur.nrm[b]);
-    const bool valid = tok_base + 4 * b + c < t_end;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      v4i acc = {0, 0, 0, 0};
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[rb][0], b0, acc, 0, 0, 0);
+      v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[rb][0], b0, bias[rb], 0, 0, 0);
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[rb][1], b1, acc, 0, 0, 0);
-      logit[rb][c][b] = valid ? n16 * fmaf(digits_value(acc), inv_q[rb], Zg[rb]) : -INFINITY;
+      logit[rb][c][b] = fmaf(fmaf(digits_value(acc), inv_q[rb], Zg[rb]), n16, 0.f);
+    }
+  }
+  if (t0 + kGroup > t_end) {   // a group cut short by max_tokens: mask the tokens beyond it
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = i >> 2, b = i & 3;
+      const bool valid = tok_base + 4 * b + c < t_end;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) logit[rb][c][b] = valid ? logit[rb][c][b] : -INFINITY;
     }
   }
 
@@ -251,9 +309,9 @@ __device__ __forceinline__ void score_phase(const GroupBytes& cur, int t0, int t
     float gm = logit[rb][0][0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) gm = fmaxf(gm, logit[rb][i >> 2][i & 3]);
-    gm = row_max16(gm);
-    const float m_new = fmaxf(st.m[rb], gm);   // finite: every group has a valid token
-    alpha[rb] = (st.m[rb] == -INFINITY) ? 0.f : exp2f(st.m[rb] - m_new);
+    gm = row_max16_ordered(gm);
+    const float m_new = (gm > st.m[rb]) ? gm : st.m[rb];   // finite: every group has a valid token
+    alpha[rb] = fast_exp2(st.m[rb] - m_new);   // 0 while m was -inf
     st.m[rb] = m_new;
     float ls = 0.f, zs = 0.f, pmax = 0.f;
     float pv[2][4];
@@ -262,25 +320,24 @@ __device__ __forceinline__ void score_phase(const GroupBytes& cur, int t0, int t
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const uint32_t w = pick(cur.vsz[b], c);
-        const float p = exp2f(logit[rb][c][b] - m_new);
+        const float p = fast_exp2(logit[rb][c][b] - m_new);
         ls += p;
         zs = fmaf(p, f16_hi(w), zs);
-        pv[c][b] = p * f16_lo(w);
+        pv[c][b] = fmaf(p, f16_lo(w), 0.f);
         pmax = fmaxf(pmax, pv[c][b]);
       }
     st.l[rb] = fmaf(st.l[rb], alpha[rb], ls);
     st.z[rb] = fmaf(st.z[rb], alpha[rb], zs);
-    pmax = row_max16(pmax);
+    pmax = row_max16_nonneg(pmax);
     int e2;
     frexpf(pmax, &e2);                       // p * vs < 2^e2 for this head and group
-    const float sc2 = ldexpf(1.f, 26 - e2);
+    const float sc2 = ldexpf(1.f, 24 - e2);
     inv_p[rb] = ldexpf(1.f, e2 - 30);
     uint32_t x[2][4];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int b = 0; b < 4; ++b)   // p * vs >= 0: +0.5 then truncation rounds to nearest
-        x[c][b] = balanced_digits(static_cast<int>(fmaf(pv[c][b], sc2 * fac[c], 0.5f)));
+      for (int b = 0; b < 4; ++b) x[c][b] = balanced_digits_off(fixed_off(pv[c][b] * (sc2 * fac[c])));
     stage_digits(sm.a_pv[wave][rb], x, gl, n);
   }
 }
@@ -293,11 +350,12 @@ __device__ __forceinline__ void value_phase(const GroupBytes& cur, Int2Smem<G>& 
                                             const float (&inv_p)[Int2Cfg<G>::kRB]) {
   constexpr int RB = Int2Cfg<G>::kRB;
   wave_sync_lds();
-  v4i ap[RB][2];
+  v4i ap[RB][2], bias[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     ap[rb][0] = read_operand(sm.a_pv[wave][rb], 0, gl, n);
     ap[rb][1] = read_operand(sm.a_pv[wave][rb], 1, gl, n);
+    bias[rb] = field3_bias(ap[rb][0], ap[rb][1]);
   }
 
 #pragma unroll
@@ -306,8 +364,7 @@ __device__ __forceinline__ void value_phase(const GroupBytes& cur, Int2Smem<G>& 
     const v4i b1 = spread_codes(cur.vd[j].y);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      v4i acc = {0, 0, 0, 0};
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap[rb][0], b0, acc, 0, 0, 0);
+      v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap[rb][0], b0, bias[rb], 0, 0, 0);
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap[rb][1], b1, acc, 0, 0, 0);
       st.acc[rb][j] = fmaf(digits_value(acc), inv_p[rb], st.acc[rb][j] * alpha[rb]);
     }
@@ -370,7 +427,7 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
       for (int b = 0; b < 4; ++b) qv[rb][c][b] = sm.u.q_rot[rb * 4 + gl][16 * (n >> 1) + 4 * b + 2 * (n & 1) + c];
   __syncthreads();  // q_rot shares storage with tail_p
   // weight divisors of the bit pairs u + c this lane's values occupy
-  const float fac[2] = {kInvWeight16[2 * (n & 1)], kInvWeight16[2 * (n & 1) + 1]};
+  const float fac[2] = {kFac[2 * (n & 1)], kFac[2 * (n & 1) + 1]};
 
   WaveRun<RB> st;
 #pragma unroll

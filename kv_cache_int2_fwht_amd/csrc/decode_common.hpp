@@ -15,17 +15,42 @@ namespace oscar {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// q [G][128] (bf16) -> dst_raw = q * scale and, if dst_rot is given,
-// dst_rot = (H q) * scale with the orthonormal Sylvester Hadamard matrix
-// (butterflies in LDS).  Rows G .. rows-1 of both are zero-filled.  Block-wide.
+// The query values a thread contributes to load_and_rotate_q: elements
+// tid and tid + blockDim.x of q [G][128] (bf16), 0 beyond G rows.  Split
+// from the rotation so that a kernel can issue these loads before other
+// long-latency loads and wait for them alone.
 template <int G, int kRows>
-__device__ void load_and_rotate_q(const uint16_t* q, float scale, float (*dst_raw)[kHeadDim],
-                                  float (*dst_rot)[kHeadDim]) {
+struct QueryRegs {
+  float v[2];
+};
+
+template <int G, int kRows>
+__device__ __forceinline__ QueryRegs<G, kRows> fetch_q(const uint16_t* q) {
+  static_assert(kRows * kHeadDim <= 2 * 512, "two query elements per thread at >= 512 threads");
+  QueryRegs<G, kRows> r;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = threadIdx.x + k * blockDim.x;
+    const float x = bf16_to_f32(q[i < G * kHeadDim ? i : 0]);   // unconditional load, no branch
+    r.v[k] = (i < G * kHeadDim) ? x : 0.f;
+  }
+  return r;
+}
+
+// dst_raw = q * scale and, if dst_rot is given, dst_rot = (H q) * scale with
+// the orthonormal Sylvester Hadamard matrix (butterflies in LDS).  Rows
+// G .. kRows-1 of both are zero-filled.  Block-wide.
+template <int G, int kRows>
+__device__ void rotate_q(const QueryRegs<G, kRows>& r, float scale, float (*dst_raw)[kHeadDim],
+                         float (*dst_rot)[kHeadDim]) {
   const int tid = threadIdx.x;
-  for (int i = tid; i < kRows * kHeadDim; i += blockDim.x) {
-    const float v = (i < G * kHeadDim) ? bf16_to_f32(q[i]) : 0.f;
-    dst_raw[i / kHeadDim][i % kHeadDim] = v * scale;
-    if (dst_rot) dst_rot[i / kHeadDim][i % kHeadDim] = v;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = tid + k * blockDim.x;
+    if (i < kRows * kHeadDim) {
+      dst_raw[i / kHeadDim][i % kHeadDim] = r.v[k] * scale;
+      if (dst_rot) dst_rot[i / kHeadDim][i % kHeadDim] = r.v[k];
+    }
   }
   __syncthreads();
   if (!dst_rot) return;
@@ -44,6 +69,13 @@ __device__ void load_and_rotate_q(const uint16_t* q, float scale, float (*dst_ra
   const float norm = scale * 0.088388347648318440550f;  // 1/sqrt(128)
   for (int i = tid; i < G * kHeadDim; i += blockDim.x) dst_rot[i / kHeadDim][i % kHeadDim] *= norm;
   __syncthreads();
+}
+
+// fetch_q followed by rotate_q.
+template <int G, int kRows>
+__device__ void load_and_rotate_q(const uint16_t* q, float scale, float (*dst_raw)[kHeadDim],
+                                  float (*dst_rot)[kHeadDim]) {
+  rotate_q<G, kRows>(fetch_q<G, kRows>(q), scale, dst_raw, dst_rot);
 }
 
 // Softmax states of G heads from kSlots producers (waves, plus extra slots

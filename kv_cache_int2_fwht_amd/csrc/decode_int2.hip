@@ -198,6 +198,62 @@ __device__ __forceinline__ v4i read_operand(const uint8_t* blk, int half, int gl
   return *reinterpret_cast<const v4i*>(blk + (half * 4 + gl) * kOpBlock + n * kOpRow);
 }
 
+// Query set-up by one wave.  Lane l holds, for row block rb, the elements
+// 8 (l % 16) .. 8 (l % 16) + 7 of head 4 rb + l / 16 (zero for heads >= G).
+template <int G, int RB>
+__device__ __forceinline__ void fetch_q_wave(const uint16_t* q, int lane, uint4 (&raw)[RB]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int head = 4 * rb + (lane >> 4);
+    const uint4 v = reinterpret_cast<const uint4*>(q)[head < G ? 16 * head + (lane & 15) : 0];
+    raw[rb] = (head < G) ? v : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// q_raw = q * scale and q_rot = (H q) * scale, H the orthonormal Sylvester
+// Hadamard matrix of order 128 in natural order: butterflies (x, y) ->
+// (x + y, x - y) over index pairs differing in one bit, the three low bits
+// inside a lane, the four high bits across the 16 lanes of a row.
+template <int RB>
+__device__ __forceinline__ void rotate_q_wave(const uint4 (&raw)[RB], float scale, float (*q_raw)[kHeadDim],
+                                              float (*q_rot)[kHeadDim], int lane) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = 4 * rb + (lane >> 4);
+    const int d0 = 8 * (lane & 15);
+    const uint32_t w[4] = {raw[rb].x, raw[rb].y, raw[rb].z, raw[rb].w};
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = bf16lo_to_f32(w[k]);
+      x[2 * k + 1] = bf16hi_to_f32(w[k]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q_raw[row][d0 + j] = x[j] * scale;
+#pragma unroll
+    for (int bit = 1; bit < 8; bit <<= 1)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (!(j & bit)) {
+          const float a = x[j], b = x[j | bit];
+          x[j] = a + b;
+          x[j | bit] = a - b;
+        }
+#pragma unroll
+    for (int lb = 1; lb < 16; lb <<= 1) {
+      const bool upper = lane & lb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float y = __shfl_xor(x[j], lb, kWave);
+        x[j] = upper ? y - x[j] : x[j] + y;
+      }
+    }
+    const float norm = scale * 0.088388347648318440550f;   // 1/sqrt(128)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q_rot[row][d0 + j] = x[j] * norm;
+  }
+}
+
 template <int G>
 struct Int2Cfg {
   static constexpr int kRB = (G + 3) / 4;  // 16-row blocks of (head, digit) rows
@@ -405,17 +461,27 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
 
   const int g_qend = min(n_groups, nq / kGroup);   // quantized groups end here; a tail group may follow
   int g = split + wave * S;
-  // start streaming this wave's first group before the query set-up
+  // Wave 0 requests the query before any wave requests cache bytes (the
+  // barrier orders the requests of the compute unit), so the query set-up
+  // does not wait behind the first groups' traffic.
+  uint4 q_in[RB];
+  if (wave == 0) fetch_q_wave<G, RB>(a.q + (static_cast<size_t>(b) * a.num_q_heads + qh0) * kHeadDim, lane, q_in);
+  __syncthreads();
+  // The first group's loads are issued without a branch (a wave without a
+  // group reads group 0 of its slice, which always exists, and ignores it),
+  // so that wave 0's wait for the query counts exactly the loads issued
+  // after it.
   GroupBytes cur;
-  if (g < g_qend) {
-    load_score_side(cur, a, slice, groups_cap, g, lane);
-    load_value_side(cur, a, slice, groups_cap, g, lane);
+  {
+    const int g_first = (g < g_qend) ? g : 0;
+    load_score_side(cur, a, slice, groups_cap, g_first, lane);
+    load_value_side(cur, a, slice, groups_cap, g_first, lane);
   }
 
-  if (wave == 0) clear_slot(sm.merge, C::kWaves);  // the tail slot stays empty unless a tail is seen
-  if (tid == 0) sm.next_group = C::kWaves;   // next group index k (group split + k S); published by the barriers below
-  load_and_rotate_q<G, C::kRows>(a.q + (static_cast<size_t>(b) * a.num_q_heads + qh0) * kHeadDim,
-                                 a.sm_scale * kLog2e, sm.q_raw, sm.u.q_rot);
+  if (wave == 0) rotate_q_wave<RB>(q_in, a.sm_scale * kLog2e, sm.q_raw, sm.u.q_rot, lane);
+  if (wave == 1) clear_slot(sm.merge, C::kWaves);  // the tail slot stays empty unless a tail is seen
+  if (tid == 0) sm.next_group = C::kWaves;   // next group index k (group split + k S); published by the barrier below
+  __syncthreads();
 
   // rotated query of this lane's head and channels 16w + 4b + u + c, per row block
   float qv[RB][2][4];

@@ -268,15 +268,14 @@ struct Int2Cfg {
 template <int G>
 struct Int2Smem {
   float q_raw[Int2Cfg<G>::kRows][kHeadDim];   // q * sm_scale * log2(e)
-  union {
-    float q_rot[Int2Cfg<G>::kRows][kHeadDim];  // (H q) * sm_scale * log2(e); read once at the start
-    float tail_p[G][kGroup];                    // softmax weights of the bf16 tail tokens
-  } u;
+  float q_rot[Int2Cfg<G>::kRows][kHeadDim];   // (H q) * sm_scale * log2(e)
+  float tail_p[G][kGroup];                     // softmax weights of the bf16 tail tokens
   // per wave and row block: MFMA A operands staged as [half][lane group][row][16 bytes]
   uint8_t a_qk[Int2Cfg<G>::kWaves][Int2Cfg<G>::kRB][2 * 4 * kOpBlock];
   uint8_t a_pv[Int2Cfg<G>::kWaves][Int2Cfg<G>::kRB][2 * 4 * kOpBlock];
   MergeSmem<G, Int2Cfg<G>::kSlots> merge;
   int next_group;   // next group of this split not yet claimed by a wave
+  int q_ready;      // set by wave 0 once q_raw, q_rot, next_group and the tail slot are written
 };
 
 // Running softmax state of one wave: per row block, m (uniform over the
@@ -462,26 +461,31 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
   const int g_qend = min(n_groups, nq / kGroup);   // quantized groups end here; a tail group may follow
   int g = split + wave * S;
   // Wave 0 requests the query before any wave requests cache bytes (the
-  // barrier orders the requests of the compute unit), so the query set-up
-  // does not wait behind the first groups' traffic.
+  // barrier orders the requests of the compute unit).  It then sets up the
+  // query and the shared state and raises q_ready before requesting its own
+  // first group, while the other waves request their first groups at once
+  // and wait for q_ready only afterwards: no wave's start waits for another
+  // wave's cache requests to be accepted.
   uint4 q_in[RB];
   if (wave == 0) fetch_q_wave<G, RB>(a.q + (static_cast<size_t>(b) * a.num_q_heads + qh0) * kHeadDim, lane, q_in);
+  if (tid == 0) sm.q_ready = 0;
   __syncthreads();
-  // The first group's loads are issued without a branch (a wave without a
-  // group reads group 0 of its slice, which always exists, and ignores it),
-  // so that wave 0's wait for the query counts exactly the loads issued
-  // after it.
+  const int g_first = (g < g_qend) ? g : 0;
   GroupBytes cur;
-  {
-    const int g_first = (g < g_qend) ? g : 0;
-    load_score_side(cur, a, slice, groups_cap, g_first, lane);
-    load_value_side(cur, a, slice, groups_cap, g_first, lane);
+  if (wave == 0) {
+    rotate_q_wave<RB>(q_in, a.sm_scale * kLog2e, sm.q_raw, sm.q_rot, lane);
+    clear_slot(sm.merge, C::kWaves);  // the tail slot stays empty unless a tail is seen
+    if (lane == 0) sm.next_group = C::kWaves;   // next group index k (group split + k S)
+    // every lane releases its own writes
+    __hip_atomic_store(&sm.q_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
-
-  if (wave == 0) rotate_q_wave<RB>(q_in, a.sm_scale * kLog2e, sm.q_raw, sm.u.q_rot, lane);
-  if (wave == 1) clear_slot(sm.merge, C::kWaves);  // the tail slot stays empty unless a tail is seen
-  if (tid == 0) sm.next_group = C::kWaves;   // next group index k (group split + k S); published by the barrier below
-  __syncthreads();
+  // The first group's loads are issued without a branch on the group (a wave
+  // without a group reads group 0 of its slice, which always exists, and
+  // ignores it), so that later waits count exactly the loads issued.
+  load_score_side(cur, a, slice, groups_cap, g_first, lane);
+  load_value_side(cur, a, slice, groups_cap, g_first, lane);
+  while (__hip_atomic_load(&sm.q_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+    __builtin_amdgcn_s_sleep(1);
 
   // rotated query of this lane's head and channels 16w + 4b + u + c, per row block
   float qv[RB][2][4];
@@ -490,8 +494,7 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) qv[rb][c][b] = sm.u.q_rot[rb * 4 + gl][16 * (n >> 1) + 4 * b + 2 * (n & 1) + c];
-  __syncthreads();  // q_rot shares storage with tail_p
+      for (int b = 0; b < 4; ++b) qv[rb][c][b] = sm.q_rot[rb * 4 + gl][16 * (n >> 1) + 4 * b + 2 * (n & 1) + c];
   // weight divisors of the bit pairs u + c this lane's values occupy
   const float fac[2] = {kFac[2 * (n & 1)], kFac[2 * (n & 1) + 1]};
 
@@ -544,7 +547,7 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
   if (nt > 0 && g_tail < n_groups && g_tail % S == split && wave == (g_tail / S) % C::kWaves) {
     const int n_tok = min(nt, total - g_tail * kGroup);
     bf16_tokens_wave<G, C::kSlots>(a.k_tail + slice * kGroup * kHeadDim, a.v_tail + slice * kGroup * kHeadDim,
-                                   n_tok, sm.q_raw, sm.u.tail_p, sm.merge, C::kWaves);
+                                   n_tok, sm.q_raw, sm.tail_p, sm.merge, C::kWaves);
   }
 
   const size_t partial_base = (static_cast<size_t>(b) * a.num_q_heads + qh0) * a.splits;

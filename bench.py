@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target seconds of oracle work")
     p.add_argument("--profile", choices=["none", "int2", "bf16", "quantize", "copy"], default="none",
                    help="run only one kernel (for rocprofv3 runs) and print its timing")
+    p.add_argument("--sweep", action="store_true",
+                   help="context sweep 8K..128K at batch 1 and 8: INT2 and bf16 decode steps, speed-up and "
+                        "cache footprint (one JSON line per configuration instead of the benchmark line)")
     return p.parse_args()
 
 
@@ -106,6 +109,89 @@ def cpu_baseline(target_s):
                       f"{reps} repetitions in {el:.1f} s; GB/s = algorithmic bytes of those steps / time"}
 
 
+def context_sweep(args):
+    """Decode-step time of the INT2 path and of the bf16 kernel for contexts
+    8K..128K at batch 1 and 8 (Llama-3.1-8B layer shape).  Keys and values
+    of the 8 KV heads come from the 128K generator and are reused for every
+    sequence of a batch (the step time does not depend on the values).
+    Enough cache copies are cycled that at least 512 MB is read between
+    repeats of the same copy."""
+    import numpy as np
+    import torch
+    import synthetic as syn
+    from kv_cache_int2_fwht_amd import binding as ob
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    w = syn.workload(3)
+    H, Hq, Tmax = w.num_kv_heads, w.num_q_heads, w.lengths[0]
+    sm = 1.0 / np.sqrt(128.0)
+    src_k = torch.empty((H, Tmax, 128), dtype=torch.bfloat16, device=dev)
+    src_v = torch.empty_like(src_k)
+    for h in range(H):
+        src_k[h] = torch.from_numpy(syn.keys_slice(w, 0, h).view(np.int16)).to(dev).view(torch.bfloat16)
+        src_v[h] = torch.from_numpy(syn.values_slice(w, 0, h).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    for B in (1, 8):
+        q = torch.from_numpy(np.stack([syn.query(w, 0)] * B).view(np.int16)).to(dev).view(torch.bfloat16).contiguous()
+        out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+        for T in (8192, 16384, 32768, 65536, 131072):
+            k = src_k[:, :T].unsqueeze(0).expand(B, H, T, 128).contiguous()
+            v = src_v[:, :T].unsqueeze(0).expand(B, H, T, 128).contiguous()
+            int2_cache_bytes = B * H * T * BYTES_PER_TOKEN_HEAD
+            bf16_cache_bytes = B * H * T * BF16_BYTES_PER_TOKEN_HEAD
+            n_int2 = min(64, max(1, -(-(512 << 20) // int2_cache_bytes)))
+            n_bf16 = min(16, max(1, -(-(512 << 20) // bf16_cache_bytes)))
+            caches = [ob.PackedCache(B, H, T, device=dev) for _ in range(n_int2)]
+            ob.quantize_kv(caches[0], k, v, torch.zeros(B, dtype=torch.int32, device=dev),
+                           torch.full((B,), T // 128, dtype=torch.int32, device=dev), T // 128)
+            for c in caches[1:]:
+                for name in ("k_codes", "k_sz", "k_norm", "v_codes", "v_sz"):
+                    getattr(c, name).copy_(getattr(caches[0], name))
+            kv = [(k, v)] + [(k.clone(), v.clone()) for _ in range(n_bf16 - 1)]
+            del k, v
+            nq = torch.full((B,), T, dtype=torch.int32, device=dev)
+            nt = torch.zeros(B, dtype=torch.int32, device=dev)
+            ws = ob.alloc_workspace(B, H, Hq, T, device=dev)
+
+            def int2_step(i):
+                ob.decode_attn(caches[i % n_int2], nq, nt, T, q, sm, out, ws, stream=stream)
+
+            def bf16_step(i):
+                kk, vv = kv[i % n_bf16]
+                ob.decode_attn_bf16(kk, vv, nq, T, q, sm, out, ws, stream=stream)
+
+            for i in range(10):
+                int2_step(i)
+                bf16_step(i)
+            int2_us = timed(int2_step, max(20, args.steps // 4))
+            bf16_us = timed(bf16_step, max(10, args.steps // 10))
+            int2_alg = int2_cache_bytes + B * Hq * 128 * 6
+            bf16_alg = bf16_cache_bytes + B * Hq * 128 * 6
+            print(json.dumps({"batch": B, "context": T, "int2_us": round(int2_us, 2), "bf16_us": round(bf16_us, 2),
+                              "speedup": round(bf16_us / int2_us, 3),
+                              "int2_GBs": round(int2_alg / (int2_us * 1e-6) / 1e9, 1),
+                              "bf16_GBs": round(bf16_alg / (bf16_us * 1e-6) / 1e9, 1),
+                              "tokens_per_s_int2": round(B / (int2_us * 1e-6), 1),
+                              "tokens_per_s_bf16": round(B / (bf16_us * 1e-6), 1),
+                              "cache_bytes_int2": int2_cache_bytes, "cache_bytes_bf16": bf16_cache_bytes,
+                              "footprint_ratio": round(bf16_cache_bytes / int2_cache_bytes, 3),
+                              "copies": [n_int2, n_bf16]}), flush=True)
+            del caches, kv, ws
+            torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -113,6 +199,10 @@ def main():
               "(the decode shards by KV head, sequence or batch without a collective on the hot path)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        context_sweep(args)
+        return
 
     import numpy as np
     import torch

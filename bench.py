@@ -109,6 +109,28 @@ def cpu_baseline(target_s):
                       f"{reps} repetitions in {el:.1f} s; GB/s = algorithmic bytes of those steps / time"}
 
 
+def graph_step_us(calls, replays):
+    """Per-call GPU time of `calls` (functions that launch on the current
+    stream) captured once in a HIP graph and replayed `replays` times: the
+    step time without the host's per-call submission cost."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for fn in calls:
+            fn()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (replays * len(calls))
+
+
 def context_sweep(args):
     """Decode-step time of the INT2 path and of the bf16 kernel for contexts
     8K..128K at batch 1 and 8 (Llama-3.1-8B layer shape).  Keys and values
@@ -177,9 +199,12 @@ def context_sweep(args):
                 bf16_step(i)
             int2_us = timed(int2_step, max(20, args.steps // 4))
             bf16_us = timed(bf16_step, max(10, args.steps // 10))
+            int2_graph_us = graph_step_us(
+                [lambda c=c: ob.decode_attn(c, nq, nt, T, q, sm, out, ws) for c in caches], max(2, 64 // n_int2))
             int2_alg = int2_cache_bytes + B * Hq * 128 * 6
             bf16_alg = bf16_cache_bytes + B * Hq * 128 * 6
-            print(json.dumps({"batch": B, "context": T, "int2_us": round(int2_us, 2), "bf16_us": round(bf16_us, 2),
+            print(json.dumps({"batch": B, "context": T, "int2_us": round(int2_us, 2),
+                              "int2_us_graph": round(int2_graph_us, 2), "bf16_us": round(bf16_us, 2),
                               "speedup": round(bf16_us / int2_us, 3),
                               "int2_GBs": round(int2_alg / (int2_us * 1e-6) / 1e9, 1),
                               "bf16_GBs": round(bf16_alg / (bf16_us * 1e-6) / 1e9, 1),
@@ -301,6 +326,9 @@ def main():
     for i in range(args.warmup):
         int2_kernel(i)
     kern_us, kern_med_us = timed_each(int2_kernel, args.steps)
+    # the same steps replayed from a HIP graph (no per-call host cost)
+    int2_graph_us = graph_step_us([lambda c=c: ob.decode_attn(c, nq, nt, T, q, sm, out, ws) for c in caches],
+                                  max(2, args.steps // len(caches)))
 
     # ---- bf16 flash-decoding on identical unquantized K/V ----
     kv_copies = [(k_src, v_src)] + [(k_src.clone(), v_src.clone()) for _ in range(max(0, args.bf16_copies - 1))]
@@ -338,6 +366,7 @@ def main():
         "config": {"workload": "llama31-8b-layer-128k", "batch": B, "q_heads": Hq, "kv_heads": H,
                    "head_dim": 128, "context": T, "tail": 0, "cache_copies": len(caches)},
         "us_per_step": round(int2_us, 3),
+        "us_per_step_graph_replay": round(int2_graph_us, 3),
         "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(B / (int2_us * 1e-6), 1),
         "roofline": {"bound": "hbm", "achieved": round(kern_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

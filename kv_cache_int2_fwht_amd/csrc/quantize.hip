@@ -11,7 +11,12 @@
 // KV head).  Every quantity that decides an fp16 parameter or a code is
 // computed in fp64: the Hadamard butterflies on bf16 inputs are then exact
 // in practice, so the stored norms, scales, zero-points and codes are the
-// ones an fp64 evaluation of the same formulas gives.
+// ones an fp64 evaluation of the same formulas gives.  The keys are read
+// twice (the second time from cache): the first pass finds norms and
+// per-channel ranges, the second repeats the identical transform and writes
+// the codes, so no lane has to keep a whole token's fp64 row alive across
+// the block-wide reduction.  The group's values are kept in LDS between
+// their two passes.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -25,13 +30,66 @@ __device__ __forceinline__ uint32_t code_from(double x, double z, double s, doub
   // inv_s == 0 encodes s == 0: r = 0 and the code is 0.
   double r = (x - z) * inv_s;
   // Within a hair of a half-way point the reciprocal product can land on the
-  // other side of an exact tie; decide those with the correctly rounded quotient.
-  if (fabs((r - floor(r)) - 0.5) < 1e-9 && s > 0.0) r = (x - z) / s;
+  // other side of an exact tie; decide those with the correctly rounded
+  // quotient.  Such values are rare, so the division runs only in waves that
+  // hold one.
+  const bool near_tie = fabs((r - floor(r)) - 0.5) < 1e-9 && s > 0.0;
+  if (__any(near_tie)) {
+    if (near_tie) r = (x - z) / s;
+  }
   const double c = fmin(fmax(rint(r), 0.0), 3.0);
   return static_cast<uint32_t>(c);
 }
 
-__global__ __launch_bounds__(kThreads) void quantize_kv_kernel(QuantizeArgs a) {
+// 32 channels 32L .. 32L+31 of one key row (bf16) -> the unnormalised
+// Walsh-Hadamard transform Y = sqrt(128) H k in fp64 across the four lanes
+// L = 0..3 of a quad: channel bits 0..4 in-lane, bits 5 and 6 across the
+// quad (exact for bf16 inputs in practice).
+__device__ __forceinline__ void key_fwht(const uint16_t* row, int L, double (&x)[32]) {
+  const uint4* src = reinterpret_cast<const uint4*>(row + 32 * L);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 w = src[q];
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[8 * q + 2 * e] = static_cast<double>(bf16lo_to_f32(ws[e]));
+      x[8 * q + 2 * e + 1] = static_cast<double>(bf16hi_to_f32(ws[e]));
+    }
+  }
+#pragma unroll
+  for (int bit = 1; bit < 32; bit <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (!(i & bit)) {
+        const double p = x[i], r = x[i | bit];
+        x[i] = p + r;
+        x[i | bit] = p - r;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const double p = dpp_f64<kDppQuadXor1>(x[i]);
+    x[i] = (L & 1) ? (p - x[i]) : (x[i] + p);
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const double p = dpp_f64<kDppQuadXor2>(x[i]);
+    x[i] = (L & 2) ? (p - x[i]) : (x[i] + p);
+  }
+}
+
+struct QuantSmem {
+  double red_min[16][kHeadDim];   // per-channel min / max of the scaled keys, one row per (wave, 16-lane row)
+  double red_max[16][kHeadDim];
+  double zs[kHeadDim], ss[kHeadDim], inv_s[kHeadDim];   // key (z16, s16, 1 / s16) per channel
+  double inv_n[kGroup];                                  // 1 / (sqrt(128) n16) per token (0 if n16 = 0)
+  double vz[kGroup], vs[kGroup], vinv[kGroup];           // value (z16, s16, 1 / s16) per token
+  uint4 vrow[kGroup][kHeadDim / 8];                      // the group's values (bf16)
+};
+
+__global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a) {
   const int j = blockIdx.x;   // source group
   const int h = blockIdx.y;   // KV head
   const int b = blockIdx.z;   // sequence
@@ -49,60 +107,19 @@ __global__ __launch_bounds__(kThreads) void quantize_kv_kernel(QuantizeArgs a) {
   const uint16_t* ksrc = a.k_src + b * a.sb + h * a.sh + static_cast<int64_t>(j) * kGroup * a.st;
   const uint16_t* vsrc = a.v_src + b * a.sb + h * a.sh + static_cast<int64_t>(j) * kGroup * a.st;
 
-  __shared__ double red_min[16][kHeadDim];
-  __shared__ double red_max[16][kHeadDim];
-  __shared__ double zs[kHeadDim];
-  __shared__ double ss[kHeadDim];
-  __shared__ double inv_s[kHeadDim];
-  __shared__ double vz[kGroup];
-  __shared__ double vs[kGroup];
-  __shared__ double vinv[kGroup];
+  __shared__ QuantSmem sm;
 
-  // ---------------- keys ----------------
+  // ---------------- keys, first pass: norms and per-channel ranges ----------------
   // Lane = (slot, L): 4 lanes per token, lane L holds channels 32L..32L+31.
   // A wave covers 16 tokens per pass, two passes: tokens wave*32 + pass*16 + slot.
   const int L = lane & 3;
   const int slot = lane >> 2;
-  double u[2][32];
-  uint16_t n16_bits[2];
-#pragma unroll
+  const int row = wave * 4 + (lane >> 4);
+#pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
     const int t = wave * 32 + pass * 16 + slot;
-    const uint4* src = reinterpret_cast<const uint4*>(ksrc + static_cast<int64_t>(t) * a.st + 32 * L);
-    double* x = u[pass];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 w = src[q];
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[8 * q + 2 * e] = static_cast<double>(bf16lo_to_f32(ws[e]));
-        x[8 * q + 2 * e + 1] = static_cast<double>(bf16hi_to_f32(ws[e]));
-      }
-    }
-    // Unnormalised Walsh-Hadamard butterflies, channel bits 0..4 in-lane.
-#pragma unroll
-    for (int bit = 1; bit < 32; bit <<= 1) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (!(i & bit)) {
-          const double p = x[i], r = x[i | bit];
-          x[i] = p + r;
-          x[i | bit] = p - r;
-        }
-      }
-    }
-    // Channel bit 5 = lane bit 0, channel bit 6 = lane bit 1 (DPP within the quad).
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const double p = dpp_f64<kDppQuadXor1>(x[i]);
-      x[i] = (L & 1) ? (p - x[i]) : (x[i] + p);
-    }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const double p = dpp_f64<kDppQuadXor2>(x[i]);
-      x[i] = (L & 2) ? (p - x[i]) : (x[i] + p);
-    }
+    double x[32];
+    key_fwht(ksrc + static_cast<int64_t>(t) * a.st, L, x);
     // ||y||^2 = sum(Y^2) / 128 for the unnormalised transform Y = sqrt(128) y.
     double ssq = 0.0;
 #pragma unroll
@@ -110,65 +127,35 @@ __global__ __launch_bounds__(kThreads) void quantize_kv_kernel(QuantizeArgs a) {
     ssq += dpp_f64<kDppQuadXor1>(ssq);   // a + b == b + a: all four lanes agree
     ssq += dpp_f64<kDppQuadXor2>(ssq);
     const double n = sqrt(ssq * (1.0 / 128.0));
-    n16_bits[pass] = f64_to_f16_bits_rne_sat(n);
-    const double n16 = f16_bits_to_f64(n16_bits[pass]);
+    const uint16_t n16_bits = f64_to_f16_bits_rne_sat(n);
+    const double n16 = f16_bits_to_f64(n16_bits);
     const double inv = (n16 > 0.0) ? 1.0 / (n16 * kSqrt128) : 0.0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) x[i] *= inv;
-  }
-  // Per-channel min / max over this lane's two tokens, then over the four
-  // token slots of each 16-lane row.
-  double mn[32], mx[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    mn[i] = fmin(u[0][i], u[1][i]);
-    mx[i] = fmax(u[0][i], u[1][i]);
-    mn[i] = fmin(mn[i], dpp_f64<kDppRowRor4>(mn[i]));
-    mx[i] = fmax(mx[i], dpp_f64<kDppRowRor4>(mx[i]));
-    mn[i] = fmin(mn[i], dpp_f64<kDppRowRor8>(mn[i]));
-    mx[i] = fmax(mx[i], dpp_f64<kDppRowRor8>(mx[i]));
-  }
-  const int row = wave * 4 + (lane >> 4);
-  if ((lane & 15) < 4) {
+    if (L == 0) {
+      a.k_norm[tok0 + t] = n16_bits;
+      sm.inv_n[t] = inv;
+    }
+    // per-channel min / max over the four token slots of each 16-lane row
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      red_min[row][32 * L + i] = mn[i];
-      red_max[row][32 * L + i] = mx[i];
+      const double u = x[i] * inv;
+      double mn = fmin(u, dpp_f64<kDppRowRor4>(u));
+      double mx = fmax(u, dpp_f64<kDppRowRor4>(u));
+      mn = fmin(mn, dpp_f64<kDppRowRor8>(mn));
+      mx = fmax(mx, dpp_f64<kDppRowRor8>(mx));
+      if ((lane & 15) < 4) {
+        if (pass == 0) {
+          sm.red_min[row][32 * L + i] = mn;
+          sm.red_max[row][32 * L + i] = mx;
+        } else {   // the same lane wrote these entries in the first pass
+          sm.red_min[row][32 * L + i] = fmin(sm.red_min[row][32 * L + i], mn);
+          sm.red_max[row][32 * L + i] = fmax(sm.red_max[row][32 * L + i], mx);
+        }
+      }
     }
-  }
-  __syncthreads();
-  if (tid < kHeadDim) {
-    double lo = red_min[0][tid], hi = red_max[0][tid];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) {
-      lo = fmin(lo, red_min[r][tid]);
-      hi = fmax(hi, red_max[r][tid]);
-    }
-    const uint16_t s_bits = f64_to_f16_bits_rne_sat((hi - lo) / 3.0);
-    const uint16_t z_bits = f64_to_f16_bits_rne_sat(lo);
-    reinterpret_cast<uint32_t*>(a.k_sz)[grp * kHeadDim + tid] =
-        static_cast<uint32_t>(s_bits) | (static_cast<uint32_t>(z_bits) << 16);
-    const double s16 = f16_bits_to_f64(s_bits);
-    zs[tid] = f16_bits_to_f64(z_bits);
-    ss[tid] = s16;
-    inv_s[tid] = (s16 > 0.0) ? 1.0 / s16 : 0.0;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int t = wave * 32 + pass * 16 + slot;
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      w0 |= code_from(u[pass][i], zs[32 * L + i], ss[32 * L + i], inv_s[32 * L + i]) << (2 * i);
-      w1 |= code_from(u[pass][16 + i], zs[32 * L + 16 + i], ss[32 * L + 16 + i], inv_s[32 * L + 16 + i]) << (2 * i);
-    }
-    *reinterpret_cast<uint2*>(a.k_codes + (tok0 + t) * 32 + 8 * L) = make_uint2(w0, w1);
-    if (L == 0) a.k_norm[tok0 + t] = n16_bits[pass];
   }
 
-  // ---------------- values ----------------
-  // Statistics: 16 lanes per token, 8 channels per lane, 4 tokens per wave pass.
+  // ---------------- values, first pass: per-token ranges; rows kept in LDS ----------------
+  // 16 lanes per token, 8 channels per lane, 4 tokens per wave pass.
   {
     const int cb = lane & 15;
     const int tslot = lane >> 4;
@@ -176,6 +163,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kv_kernel(QuantizeArgs a) {
     for (int pass = 0; pass < 8; ++pass) {
       const int t = wave * 32 + pass * 4 + tslot;
       const uint4 w = *reinterpret_cast<const uint4*>(vsrc + static_cast<int64_t>(t) * a.st + 8 * cb);
+      sm.vrow[t][cb] = w;
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
       float lo = bf16lo_to_f32(ws[0]), hi = lo;
 #pragma unroll
@@ -198,31 +186,69 @@ __global__ __launch_bounds__(kThreads) void quantize_kv_kernel(QuantizeArgs a) {
         reinterpret_cast<uint32_t*>(a.v_sz)[tok0 + t] =
             static_cast<uint32_t>(s_bits) | (static_cast<uint32_t>(z_bits) << 16);
         const double s16 = f16_bits_to_f64(s_bits);
-        vz[t] = f16_bits_to_f64(z_bits);
-        vs[t] = s16;
-        vinv[t] = (s16 > 0.0) ? 1.0 / s16 : 0.0;
+        sm.vz[t] = f16_bits_to_f64(z_bits);
+        sm.vs[t] = s16;
+        sm.vinv[t] = (s16 > 0.0) ? 1.0 / s16 : 0.0;
       }
     }
   }
   __syncthreads();
-  // Codes: thread = (channel d, half of the group's tokens); one 16-byte store.
+
+  // ---------------- key parameters per channel ----------------
+  if (tid < kHeadDim) {
+    double lo = sm.red_min[0][tid], hi = sm.red_max[0][tid];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      lo = fmin(lo, sm.red_min[r][tid]);
+      hi = fmax(hi, sm.red_max[r][tid]);
+    }
+    const uint16_t s_bits = f64_to_f16_bits_rne_sat((hi - lo) / 3.0);
+    const uint16_t z_bits = f64_to_f16_bits_rne_sat(lo);
+    reinterpret_cast<uint32_t*>(a.k_sz)[grp * kHeadDim + tid] =
+        static_cast<uint32_t>(s_bits) | (static_cast<uint32_t>(z_bits) << 16);
+    const double s16 = f16_bits_to_f64(s_bits);
+    sm.zs[tid] = f16_bits_to_f64(z_bits);
+    sm.ss[tid] = s16;
+    sm.inv_s[tid] = (s16 > 0.0) ? 1.0 / s16 : 0.0;
+  }
+
+  // ---------------- value codes: thread = (channel d, half of the group's tokens) ----------------
   {
     const int d = tid & (kHeadDim - 1);
     const int half = tid >> 7;
+    const uint16_t* vr = reinterpret_cast<const uint16_t*>(&sm.vrow[0][0]);
     uint32_t words[4];
 #pragma unroll
     for (int wd = 0; wd < 4; ++wd) {
       uint32_t acc = 0;
-#pragma unroll
+#pragma unroll 4
       for (int e = 0; e < 16; ++e) {
         const int t = half * 64 + wd * 16 + e;
-        const double v = static_cast<double>(bf16_to_f32(vsrc[static_cast<int64_t>(t) * a.st + d]));
-        acc |= code_from(v, vz[t], vs[t], vinv[t]) << (2 * e);
+        const double v = static_cast<double>(bf16_to_f32(vr[t * kHeadDim + d]));
+        acc |= code_from(v, sm.vz[t], sm.vs[t], sm.vinv[t]) << (2 * e);
       }
       words[wd] = acc;
     }
     *reinterpret_cast<uint4*>(a.v_codes + (grp * kHeadDim + d) * 32 + 16 * half) =
         make_uint4(words[0], words[1], words[2], words[3]);
+  }
+  __syncthreads();
+
+  // ---------------- keys, second pass: the same transform again, then codes ----------------
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    const int t = wave * 32 + pass * 16 + slot;
+    double x[32];
+    key_fwht(ksrc + static_cast<int64_t>(t) * a.st, L, x);   // bit-identical to the first pass
+    const double inv = sm.inv_n[t];
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c0 = 32 * L + i, c1 = 32 * L + 16 + i;
+      w0 |= code_from(x[i] * inv, sm.zs[c0], sm.ss[c0], sm.inv_s[c0]) << (2 * i);
+      w1 |= code_from(x[16 + i] * inv, sm.zs[c1], sm.ss[c1], sm.inv_s[c1]) << (2 * i);
+    }
+    *reinterpret_cast<uint2*>(a.k_codes + (tok0 + t) * 32 + 8 * L) = make_uint2(w0, w1);
   }
 }
 

@@ -129,35 +129,86 @@ struct GroupBytes {
   uint2 ksz[4];     // (s | z << 16) of channels 16w + 4b + u + {0, 1}
 };
 
-// Bytes of group g needed by the score phase: key codes, norms, key scales
-// and zero-points, value scales and zero-points (used by the softmax).
-__device__ __forceinline__ void load_score_side(GroupBytes& r, const DecodeInt2Args& a, size_t slice, int groups_cap,
-                                                int g, int lane) {
-  const int gl = lane >> 4;
-  const int n = lane & 15;
-  const int base = 16 * (n >> 1) + 2 * (n & 1);   // token / channel 16w + u
+// A group's bytes in LDS, as one loader wave copies them with direct
+// global -> LDS loads (16 bytes per lane per instruction, one contiguous
+// kilobyte per wave instruction).  Compute waves read their lane's operands
+// from it (read_stage).
+constexpr int kStageK = 0;         // 4096 B: key code half rows (16 B), order given by k_slot
+constexpr int kStageV = 4096;      // 4096 B: value code rows, channel-major as in memory
+constexpr int kStageKsz = 8192;    // 512 B: (s, z) per channel
+constexpr int kStageVsz = 8704;    // 512 B: (vs, vz) per token
+constexpr int kStageNorm = 9216;   // 256 B: fp16 norms
+constexpr int kStageBytes = 9472;
+constexpr int kDmaPerGroup = 10;   // load instructions per group (the norms take one of them)
+
+// LDS slot of half row hh of token t: the XOR with bit 4 of t makes the
+// 8-byte reads of a score tile hit every bank equally often.
+__device__ __forceinline__ int k_slot(int t, int hh) { return 2 * (t ^ ((t >> 4) & 1)) + hh; }
+
+// One 16-byte-per-lane global -> LDS load: lane l's 16 bytes at gptr land at
+// LDS byte lds + 16 l (lanes switched off write nothing).  Issued as inline
+// assembly: the loader wave tracks completion with its own vector-memory
+// counter waits.
+__device__ __forceinline__ void lds_load16(const void* gptr, const uint8_t* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0)
+               : "memory");
+}
+
+// The kDmaPerGroup loads that copy group g of a slice into a stage.
+__device__ __forceinline__ void dma_group(uint8_t* stage, const DecodeInt2Args& a, size_t slice, int groups_cap,
+                                          int g, int lane) {
   const size_t row0 = slice * a.capacity + static_cast<size_t>(g) * kGroup;   // first token row
   const size_t grp = slice * groups_cap + g;
-  const uint8_t* kc = a.k_codes + (row0 + base) * 32 + 8 * gl;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r.kd[i] = *reinterpret_cast<const uint2*>(kc + (4 * (i & 3) + (i >> 2)) * 32);
+  for (int j = 0; j < 4; ++j) {
+    const int sl = 64 * j + lane;                       // stage slot this lane fills
+    const int t = (sl >> 1) ^ ((sl >> 5) & 1);          // the inverse of k_slot
+    lds_load16(a.k_codes + (row0 + t) * 32 + 16 * (sl & 1), stage + kStageK + 1024 * j);
+  }
+  const uint8_t* vsrc = a.v_codes + grp * (kHeadDim * 32) + 16 * lane;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    r.nrm[b] = *reinterpret_cast<const uint32_t*>(a.k_norm + row0 + base + 4 * b);
-    r.vsz[b] = *reinterpret_cast<const uint2*>(a.v_sz + (row0 + base + 4 * b) * 2);
-    r.ksz[b] = *reinterpret_cast<const uint2*>(a.k_sz + (grp * kHeadDim + base + 4 * b) * 2);
+  for (int j = 0; j < 4; ++j) lds_load16(vsrc + 1024 * j, stage + kStageV + 1024 * j);
+  const uint8_t* szsrc = (lane < 32) ? reinterpret_cast<const uint8_t*>(a.k_sz) + grp * 512 + 16 * lane
+                                     : reinterpret_cast<const uint8_t*>(a.v_sz) + row0 * 4 + 16 * (lane - 32);
+  lds_load16(szsrc, stage + kStageKsz);
+  const uint8_t* nsrc = reinterpret_cast<const uint8_t*>(a.k_norm) + row0 * 2 + 16 * (lane & 15);
+  if (lane < 16) lds_load16(nsrc, stage + kStageNorm);
+}
+
+// Wait until at most `rem` groups' copies of this wave are outstanding
+// (rem <= N; the counter wait takes its count as an immediate).
+template <int N>
+__device__ __forceinline__ void wait_groups_outstanding(int rem) {
+  if constexpr (N <= 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (rem >= N) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N * kDmaPerGroup) : "memory");
+    } else {
+      wait_groups_outstanding<N - 1>(rem);
+    }
   }
 }
 
-// Bytes of group g needed by the value phase: the value codes.
-__device__ __forceinline__ void load_value_side(GroupBytes& r, const DecodeInt2Args& a, size_t slice, int groups_cap,
-                                                int g, int lane) {
+// Registers of the group being computed (see the lane roles above).
+__device__ __forceinline__ void read_stage(GroupBytes& r, const uint8_t* stage, int lane) {
   const int gl = lane >> 4;
   const int n = lane & 15;
-  const size_t grp = slice * groups_cap + g;
-  const uint8_t* vc = a.v_codes + (grp * kHeadDim + n) * 32 + 8 * gl;
+  const int base = 16 * (n >> 1) + 2 * (n & 1);   // token / channel 16w + u
 #pragma unroll
-  for (int j = 0; j < 8; ++j) r.vd[j] = *reinterpret_cast<const uint2*>(vc + j * 16 * 32);
+  for (int i = 0; i < 8; ++i) {
+    const int t = base + 4 * (i & 3) + (i >> 2);
+    r.kd[i] = *reinterpret_cast<const uint2*>(stage + kStageK + 16 * k_slot(t, gl >> 1) + 8 * (gl & 1));
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r.vd[j] = *reinterpret_cast<const uint2*>(stage + kStageV + (16 * j + n) * 32 + 8 * gl);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    r.nrm[b] = *reinterpret_cast<const uint32_t*>(stage + kStageNorm + 2 * (base + 4 * b));
+    r.vsz[b] = *reinterpret_cast<const uint2*>(stage + kStageVsz + 4 * (base + 4 * b));
+    r.ksz[b] = *reinterpret_cast<const uint2*>(stage + kStageKsz + 4 * (base + 4 * b));
+  }
 }
 
 __device__ __forceinline__ uint32_t pick(const uint2& v, int c) { return c ? v.y : v.x; }
@@ -259,10 +310,17 @@ struct Int2Cfg {
   static constexpr int kRB = (G + 3) / 4;  // 16-row blocks of (head, digit) rows
   static constexpr int kRows = kRB * 4;    // heads incl. zero padding
   // One workgroup per compute unit: 12 waves (3 per SIMD) while the kernel
-  // fits in 168 VGPRs, 8 waves for 8 query heads per KV head.
+  // fits in 168 VGPRs, 8 waves for 8 query heads per KV head.  The last
+  // kLoaders waves stream the cache into LDS; the others compute.
   static constexpr int kWaves = (kRB == 1) ? 12 : 8;
+  static constexpr int kLoaders = 2;
+  static constexpr int kCompute = kWaves - kLoaders;
   static constexpr int kThreads = kWaves * kWave;
-  static constexpr int kSlots = kWaves + 1;  // waves + the bf16-tail state
+  static constexpr int kSlots = kWaves + 1;  // one merge slot per wave (the loaders' stay empty) + the bf16 tail
+  static constexpr int kRing = 12;           // group stages in LDS (a multiple of kLoaders)
+  static constexpr int kAhead = 2;           // groups each loader has in flight (kAhead * kDmaPerGroup <= 63)
+  static_assert(kRing % kLoaders == 0, "a stage is always refilled by the same loader");
+  static_assert(kAhead * kDmaPerGroup <= 63, "vector-memory counter limit");
 };
 
 template <int G>
@@ -270,12 +328,18 @@ struct Int2Smem {
   float q_raw[Int2Cfg<G>::kRows][kHeadDim];   // q * sm_scale * log2(e)
   float q_rot[Int2Cfg<G>::kRows][kHeadDim];   // (H q) * sm_scale * log2(e)
   float tail_p[G][kGroup];                     // softmax weights of the bf16 tail tokens
-  // per wave and row block: MFMA A operands staged as [half][lane group][row][16 bytes]
-  uint8_t a_qk[Int2Cfg<G>::kWaves][Int2Cfg<G>::kRB][2 * 4 * kOpBlock];
-  uint8_t a_pv[Int2Cfg<G>::kWaves][Int2Cfg<G>::kRB][2 * 4 * kOpBlock];
-  MergeSmem<G, Int2Cfg<G>::kSlots> merge;
-  int next_group;   // next group of this split not yet claimed by a wave
-  int q_ready;      // set by wave 0 once q_raw, q_rot, next_group and the tail slot are written
+  // per compute wave and row block: an MFMA A operand staged as
+  // [half][lane group][row][16 bytes] (the scores' q digits, then the
+  // values' p digits)
+  uint8_t a_op[Int2Cfg<G>::kCompute][Int2Cfg<G>::kRB][2 * 4 * kOpBlock];
+  // the ring of group stages; once every group is computed, the merge slots
+  union {
+    uint8_t ring[Int2Cfg<G>::kRing][kStageBytes];
+    MergeSmem<G, Int2Cfg<G>::kSlots> merge;
+  } u;
+  int filled[Int2Cfg<G>::kRing];    // stage s holds group index k = s + kRing * (filled[s] - 1)
+  int emptied[Int2Cfg<G>::kRing];   // times stage s has been read into registers
+  int q_ready;                      // set by wave 0 once q_raw and q_rot are written
 };
 
 // Running softmax state of one wave: per row block, m (uniform over the
@@ -322,14 +386,14 @@ __device__ __forceinline__ void score_phase(const GroupBytes& cur, int t0, int t
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int b = 0; b < 4; ++b) x[c][b] = balanced_digits_off(fixed_off(qs[c][b] * (sc * fac[c])));
-    stage_digits(sm.a_qk[wave][rb], x, gl, n);
+    stage_digits(sm.a_op[wave][rb], x, gl, n);
   }
   wave_sync_lds();
   v4i aq[RB][2], bias[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    aq[rb][0] = read_operand(sm.a_qk[wave][rb], 0, gl, n);
-    aq[rb][1] = read_operand(sm.a_qk[wave][rb], 1, gl, n);
+    aq[rb][0] = read_operand(sm.a_op[wave][rb], 0, gl, n);
+    aq[rb][1] = read_operand(sm.a_op[wave][rb], 1, gl, n);
     bias[rb] = field3_bias(aq[rb][0], aq[rb][1]);
   }
 
@@ -393,7 +457,7 @@ __device__ __forceinline__ void score_phase(const GroupBytes& cur, int t0, int t
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int b = 0; b < 4; ++b) x[c][b] = balanced_digits_off(fixed_off(pv[c][b] * (sc2 * fac[c])));
-    stage_digits(sm.a_pv[wave][rb], x, gl, n);
+    stage_digits(sm.a_op[wave][rb], x, gl, n);
   }
 }
 
@@ -408,8 +472,8 @@ __device__ __forceinline__ void value_phase(const GroupBytes& cur, Int2Smem<G>& 
   v4i ap[RB][2], bias[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    ap[rb][0] = read_operand(sm.a_pv[wave][rb], 0, gl, n);
-    ap[rb][1] = read_operand(sm.a_pv[wave][rb], 1, gl, n);
+    ap[rb][0] = read_operand(sm.a_op[wave][rb], 0, gl, n);
+    ap[rb][1] = read_operand(sm.a_op[wave][rb], 1, gl, n);
     bias[rb] = field3_bias(ap[rb][0], ap[rb][1]);
   }
 
@@ -424,7 +488,7 @@ __device__ __forceinline__ void value_phase(const GroupBytes& cur, Int2Smem<G>& 
       st.acc[rb][j] = fmaf(digits_value(acc), inv_p[rb], st.acc[rb][j] * alpha[rb]);
     }
   }
-  // the next group rewrites a_qk / a_pv only after this wave has read them
+  // the next group rewrites a_op only after this wave has read it
   wave_sync_lds();
 }
 
@@ -459,44 +523,20 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
   const int qh0 = h * G;
 
   const int g_qend = min(n_groups, nq / kGroup);   // quantized groups end here; a tail group may follow
-  int g = split + wave * S;
-  // Wave 0 requests the query before any wave requests cache bytes (the
-  // barrier orders the requests of the compute unit).  It then sets up the
-  // query and the shared state and raises q_ready before requesting its own
-  // first group, while the other waves request their first groups at once
-  // and wait for q_ready only afterwards: no wave's start waits for another
-  // wave's cache requests to be accepted.
+  // this split's quantized groups: index k is group split + k S
+  const int n_k = (g_qend > split) ? (g_qend - split + S - 1) / S : 0;
+
+  // Start-up: wave 0 requests the query first (the barrier orders the
+  // requests of the compute unit), then sets it up while the loader wave
+  // starts streaming the cache.
   uint4 q_in[RB];
   if (wave == 0) fetch_q_wave<G, RB>(a.q + (static_cast<size_t>(b) * a.num_q_heads + qh0) * kHeadDim, lane, q_in);
+  if (tid < C::kRing) {
+    sm.filled[tid] = 0;
+    sm.emptied[tid] = 0;
+  }
   if (tid == 0) sm.q_ready = 0;
   __syncthreads();
-  const int g_first = (g < g_qend) ? g : 0;
-  GroupBytes cur;
-  if (wave == 0) {
-    rotate_q_wave<RB>(q_in, a.sm_scale * kLog2e, sm.q_raw, sm.q_rot, lane);
-    clear_slot(sm.merge, C::kWaves);  // the tail slot stays empty unless a tail is seen
-    if (lane == 0) sm.next_group = C::kWaves;   // next group index k (group split + k S)
-    // every lane releases its own writes
-    __hip_atomic_store(&sm.q_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-  }
-  // The first group's loads are issued without a branch on the group (a wave
-  // without a group reads group 0 of its slice, which always exists, and
-  // ignores it), so that later waits count exactly the loads issued.
-  load_score_side(cur, a, slice, groups_cap, g_first, lane);
-  load_value_side(cur, a, slice, groups_cap, g_first, lane);
-  while (__hip_atomic_load(&sm.q_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
-    __builtin_amdgcn_s_sleep(1);
-
-  // rotated query of this lane's head and channels 16w + 4b + u + c, per row block
-  float qv[RB][2][4];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) qv[rb][c][b] = sm.q_rot[rb * 4 + gl][16 * (n >> 1) + 4 * b + 2 * (n & 1) + c];
-  // weight divisors of the bit pairs u + c this lane's values occupy
-  const float fac[2] = {kFac[2 * (n & 1)], kFac[2 * (n & 1) + 1]};
 
   WaveRun<RB> st;
 #pragma unroll
@@ -508,50 +548,111 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
     for (int j = 0; j < 8; ++j) st.acc[rb][j] = 0.f;
   }
 
-  // Groups are handed out dynamically: each wave starts with the split's
-  // group number `wave` and then claims the next unclaimed one,
-  // so waves that get fewer issue slots simply process fewer groups.  One
-  // register set per wave: the next group's score-side bytes are requested
-  // as soon as the score phase has consumed the current ones, its value
-  // codes as soon as the value phase has.
-  while (g < g_qend) {
-    float alpha[RB], inv_p[RB];
-    score_phase<G>(cur, g * kGroup, total, qv, fac, sm, st, wave, gl, n, alpha, inv_p);
-    int k_next = 0;
-    if (lane == 0) k_next = atomicAdd(&sm.next_group, 1);
-    const int g_next = split + __builtin_amdgcn_readfirstlane(k_next) * S;
-    if (g_next < g_qend) load_score_side(cur, a, slice, groups_cap, g_next, lane);
-    value_phase<G>(cur, sm, st, wave, gl, n, alpha, inv_p);
-    if (g_next < g_qend) load_value_side(cur, a, slice, groups_cap, g_next, lane);
-    g = g_next;
-  }
-
-  // ---- this wave's state -> merge slot ----
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float l_tot = row_sum16(st.l[rb]);
-    const float z_tot = row_sum16(st.z[rb]);
-    const int hh = rb * 4 + gl;
-    if (hh < G) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sm.merge.acc[wave][hh][16 * j + n] = st.acc[rb][j] + z_tot;
-      if (n == 0) {
-        sm.merge.m[wave][hh] = st.m[rb];
-        sm.merge.l[wave][hh] = l_tot;
+  if (wave >= C::kCompute) {
+    // ---- loaders: stream the split's groups through the ring ----
+    // Loader i copies the groups k = i, i + kLoaders, ...; group k goes to
+    // stage k % kRing once its previous occupant (k - kRing, the same
+    // loader's) has been read into registers.  A group is published once
+    // its copies have reached LDS, which the wave's in-order vector-memory
+    // counter shows when only the loads of the loader's kAhead - 1 later
+    // groups are still outstanding.
+    const int li = wave - C::kCompute;
+    const int n_mine = (n_k > li) ? (n_k - li + C::kLoaders - 1) / C::kLoaders : 0;
+    for (int j = 0; j < n_mine; ++j) {
+      const int k = li + j * C::kLoaders;
+      const int s = k % C::kRing;
+      const int use = k / C::kRing;   // earlier occupants of the stage
+      while (__hip_atomic_load(&sm.emptied[s], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < use)
+        __builtin_amdgcn_s_sleep(1);
+      dma_group(sm.u.ring[s], a, slice, groups_cap, split + k * S, lane);
+      if (j >= C::kAhead - 1) {
+        // the counter wait is the release: the copies are in LDS before the
+        // flag store issues (a release store would wait for every load)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((C::kAhead - 1) * kDmaPerGroup) : "memory");
+        const int kp = k - (C::kAhead - 1) * C::kLoaders;
+        __hip_atomic_store(&sm.filled[kp % C::kRing], kp / C::kRing + 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
       }
+    }
+    // the last groups: each is published as soon as its own copies are done
+    for (int j = max(n_mine - (C::kAhead - 1), 0); j < n_mine; ++j) {
+      wait_groups_outstanding<C::kAhead - 2>(n_mine - 1 - j);
+      const int kp = li + j * C::kLoaders;
+      __hip_atomic_store(&sm.filled[kp % C::kRing], kp / C::kRing + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (wave == 0) {
+      rotate_q_wave<RB>(q_in, a.sm_scale * kLog2e, sm.q_raw, sm.q_rot, lane);
+      // every lane releases its own writes
+      __hip_atomic_store(&sm.q_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    while (__hip_atomic_load(&sm.q_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+      __builtin_amdgcn_s_sleep(1);
+    // rotated query of this lane's head and channels 16w + 4b + u + c, per row block
+    float qv[RB][2][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) qv[rb][c][b] = sm.q_rot[rb * 4 + gl][16 * (n >> 1) + 4 * b + 2 * (n & 1) + c];
+    // weight divisors of the bit pairs u + c this lane's values occupy
+    const float fac[2] = {kFac[2 * (n & 1)], kFac[2 * (n & 1) + 1]};
+
+    // ---- compute waves: wave w takes the groups k = w, w + W, w + 2W, ...
+    // (W compute waves); a fixed assignment keeps the summation order, and
+    // so the result, the same from run to run ----
+    GroupBytes cur;
+    for (int k = wave; k < n_k; k += C::kCompute) {
+      const int s = k % C::kRing;
+      const int use = k / C::kRing;
+      while (__hip_atomic_load(&sm.filled[s], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <= use)
+        __builtin_amdgcn_s_sleep(1);
+      read_stage(cur, sm.u.ring[s], lane);
+      // the stage may be refilled once every lane's reads have returned
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __hip_atomic_store(&sm.emptied[s], use + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const int g = split + k * S;
+      float alpha[RB], inv_p[RB];
+      score_phase<G>(cur, g * kGroup, total, qv, fac, sm, st, wave, gl, n, alpha, inv_p);
+      value_phase<G>(cur, sm, st, wave, gl, n, alpha, inv_p);
     }
   }
 
+  // ---- every wave's state -> its merge slot (the slots replace the ring) ----
+  __syncthreads();
+  if (wave >= C::kCompute) {
+    clear_slot(sm.u.merge, wave);
+    if (wave == C::kCompute) clear_slot(sm.u.merge, C::kWaves);   // the tail slot stays empty unless a tail is seen
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float l_tot = row_sum16(st.l[rb]);
+      const float z_tot = row_sum16(st.z[rb]);
+      const int hh = rb * 4 + gl;
+      if (hh < G) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sm.u.merge.acc[wave][hh][16 * j + n] = st.acc[rb][j] + z_tot;
+        if (n == 0) {
+          sm.u.merge.m[wave][hh] = st.m[rb];
+          sm.u.merge.l[wave][hh] = l_tot;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
   // ---- the bf16 tail (at most one partial group, after the quantized ones) ----
   const int g_tail = nq / kGroup;
-  if (nt > 0 && g_tail < n_groups && g_tail % S == split && wave == (g_tail / S) % C::kWaves) {
+  if (nt > 0 && g_tail < n_groups && g_tail % S == split && wave == 0) {
     const int n_tok = min(nt, total - g_tail * kGroup);
     bf16_tokens_wave<G, C::kSlots>(a.k_tail + slice * kGroup * kHeadDim, a.v_tail + slice * kGroup * kHeadDim,
-                                   n_tok, sm.q_raw, sm.tail_p, sm.merge, C::kWaves);
+                                   n_tok, sm.q_raw, sm.tail_p, sm.u.merge, C::kWaves);
   }
 
   const size_t partial_base = (static_cast<size_t>(b) * a.num_q_heads + qh0) * a.splits;
-  write_partial<G, C::kSlots>(sm.merge, a.partials, partial_base, split, a.splits);
+  write_partial<G, C::kSlots>(sm.u.merge, a.partials, partial_base, split, a.splits);
 }
 
 template <int G>

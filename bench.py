@@ -58,8 +58,9 @@ def parse():
 def kernel_sha():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "kv_cache_int2_fwht_amd", "csrc")
-    for name in ("decode_int2.hip", "decode_common.hpp", "device_common.hpp", "internal.hpp"):
-        with open(os.path.join(csrc, name), "rb") as f:
+    for path in [os.path.join(csrc, n) for n in ("decode_int2.hip", "decode_common.hpp", "device_common.hpp",
+                                                 "internal.hpp")] + [os.path.join(ROOT, "include", "oscar.h")]:
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -179,8 +180,7 @@ def context_sweep(args):
             ob.quantize_kv(caches[0], k, v, torch.zeros(B, dtype=torch.int32, device=dev),
                            torch.full((B,), T // 128, dtype=torch.int32, device=dev), T // 128)
             for c in caches[1:]:
-                for name in ("k_codes", "k_sz", "k_norm", "v_codes", "v_sz"):
-                    getattr(c, name).copy_(getattr(caches[0], name))
+                c.blocks.copy_(caches[0].blocks)
             kv = [(k, v)] + [(k.clone(), v.clone()) for _ in range(n_bf16 - 1)]
             del k, v
             nq = torch.full((B,), T, dtype=torch.int32, device=dev)
@@ -300,8 +300,7 @@ def main():
     torch.cuda.synchronize()
     quant_us = timed(lambda i: quantize_into(caches[0]), 3 if args.profile == "none" else 1)
     for c in caches[1:]:
-        for name in ("k_codes", "k_sz", "k_norm", "v_codes", "v_sz"):
-            getattr(c, name).copy_(getattr(caches[0], name))
+        c.blocks.copy_(caches[0].blocks)
     torch.cuda.synchronize()
     if args.profile == "quantize":
         print(json.dumps({"profile": "quantize", "us_per_call": quant_us}))

@@ -32,24 +32,32 @@
  *  - fp16 and bf16 numbers are passed as uint16_t bit patterns.
  *  - head_dim and the quantization group are both fixed at 128.
  *
- * Packed cache layout (per sequence b and KV head h; the pages fix only
- * "INT2", the byte layout is this library's):
+ * Packed cache layout (the pages fix only "INT2"; the byte layout is this
+ * library's):
  *  - 2-bit codes, four per byte, least significant bits first:
  *    byte = c0 | c1 << 2 | c2 << 4 | c3 << 6.
- *  - k_codes : uint8 [batch][num_kv_heads][capacity][32]; byte i of a token
- *              row holds channels 4i..4i+3 of the rotated, scaled key.
- *  - k_sz    : fp16 [batch][num_kv_heads][capacity/128][128][2]; per group
- *              and channel the pair (scale s, zero-point z).
- *  - k_norm  : fp16 [batch][num_kv_heads][capacity]; per-token L2 norm.
- *  - v_codes : uint8 [batch][num_kv_heads][capacity/128][128][32]; per
- *              group, one 32-byte row per channel, byte j holds tokens
- *              4j..4j+3 of the group.
- *  - v_sz    : fp16 [batch][num_kv_heads][capacity][2]; per token (s, z).
+ *  - blocks : uint8 [batch][num_kv_heads][capacity/128][OSCAR_BLOCK_BYTES];
+ *             one 9472-byte block per group of 128 tokens, which holds
+ *             everything a decode step reads for that group, so that the
+ *             step streams whole blocks:
+ *      [OSCAR_BLOCK_K_CODES, +4096) key codes, [128 tokens][32 bytes]; byte
+ *                               i of a token row holds channels 4i..4i+3 of
+ *                               the rotated, scaled key;
+ *      [OSCAR_BLOCK_V_CODES, +4096) value codes, [128 channels][32 bytes];
+ *                               byte j of a channel row holds tokens
+ *                               4j..4j+3 of the group;
+ *      [OSCAR_BLOCK_K_SZ, +512)    fp16 [128 channels][2]: the group's key
+ *                               (scale s, zero-point z) per channel;
+ *      [OSCAR_BLOCK_V_SZ, +512)    fp16 [128 tokens][2]: each token's value
+ *                               (s, z);
+ *      [OSCAR_BLOCK_K_NORM, +256)  fp16 [128 tokens]: each key's L2 norm
+ *                               (after the rotation, which keeps it).
  *  - k_tail, v_tail : bf16 [batch][num_kv_heads][128][128]; the tokens of
  *              the current, not yet complete group (at most 127 are read).
  *  Dequantization: key (rotated domain) = n * (s * c + z) with the group's
  *  (s, z) for that channel; value = s * c + z with the token's (s, z).
- *  All pointers must be 16-byte aligned.
+ *  blocks must be 256-byte aligned (every block then is), the tails
+ *  16-byte aligned.
  */
 #ifndef OSCAR_H
 #define OSCAR_H
@@ -61,9 +69,17 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 1
+#define OSCAR_ABI_VERSION 2
 #define OSCAR_HEAD_DIM 128
 #define OSCAR_GROUP 128
+
+/* One group's block in the packed cache (byte offsets, see the layout above). */
+#define OSCAR_BLOCK_K_CODES 0
+#define OSCAR_BLOCK_V_CODES 4096
+#define OSCAR_BLOCK_K_SZ 8192
+#define OSCAR_BLOCK_V_SZ 8704
+#define OSCAR_BLOCK_K_NORM 9216
+#define OSCAR_BLOCK_BYTES 9472
 
 typedef enum oscar_status {
   OSCAR_OK = 0,
@@ -80,11 +96,7 @@ typedef struct oscar_kv_cache {
   int32_t head_dim;        /* must be 128 */
   int32_t group;           /* must be 128 */
   int32_t capacity;        /* tokens per sequence; a positive multiple of 128 */
-  uint8_t* k_codes;
-  uint16_t* k_sz;
-  uint16_t* k_norm;
-  uint8_t* v_codes;
-  uint16_t* v_sz;
+  uint8_t* blocks;          /* [batch][num_kv_heads][capacity/128][OSCAR_BLOCK_BYTES] */
   const uint16_t* k_tail;  /* read by oscar_decode_attn only; may be NULL if no tail is ever used */
   const uint16_t* v_tail;
 } oscar_kv_cache;

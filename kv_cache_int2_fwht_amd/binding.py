@@ -16,6 +16,9 @@ import torch
 
 HEAD_DIM = 128
 GROUP = 128
+# one group's block in the packed cache (byte offsets; include/oscar.h)
+BLOCK_K_CODES, BLOCK_V_CODES, BLOCK_K_SZ, BLOCK_V_SZ, BLOCK_K_NORM = 0, 4096, 8192, 8704, 9216
+BLOCK_BYTES = 9472
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "liboscar.so")
 _lib = None
@@ -37,11 +40,7 @@ class KVCacheDesc(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("group", ctypes.c_int32),
         ("capacity", ctypes.c_int32),
-        ("k_codes", ctypes.c_void_p),
-        ("k_sz", ctypes.c_void_p),
-        ("k_norm", ctypes.c_void_p),
-        ("v_codes", ctypes.c_void_p),
-        ("v_sz", ctypes.c_void_p),
+        ("blocks", ctypes.c_void_p),
         ("k_tail", ctypes.c_void_p),
         ("v_tail", ctypes.c_void_p),
     ]
@@ -129,13 +128,16 @@ def last_error() -> str:
 
 
 class PackedCache:
-    """Caller-owned packed cache buffers (torch tensors) and their descriptor.
+    """Caller-owned packed cache (torch tensors) and its descriptor.
 
-    Shapes (B = batch, H = KV heads, C = capacity):
-      k_codes uint8 [B,H,C,32]      k_sz int16 [B,H,C/128,128,2] (fp16 bits)
-      k_norm int16 [B,H,C] (fp16)   v_codes uint8 [B,H,C/128,128,32]
-      v_sz int16 [B,H,C,2] (fp16)   k_tail / v_tail bf16 [B,H,128,128]
-    fp16 data is held in int16 tensors so that the bit patterns are exact.
+    ``blocks`` is uint8 [B, H, C/128, 9472] (B = batch, H = KV heads,
+    C = capacity): one block per group of 128 tokens.  The fields are views
+    into it, one group per index of dimension 2:
+      k_codes uint8 [B,H,G,128,32]   k_sz int16 [B,H,G,128,2] (fp16 bits)
+      v_codes uint8 [B,H,G,128,32]   v_sz int16 [B,H,G,128,2] (fp16)
+      k_norm  int16 [B,H,G,128] (fp16)
+    fp16 data is viewed as int16 so that the bit patterns are exact.
+    k_tail / v_tail are bf16 [B,H,128,128].
     """
 
     def __init__(self, batch: int, num_kv_heads: int, capacity: int, device="cuda"):
@@ -144,26 +146,47 @@ class PackedCache:
         B, H, C = batch, num_kv_heads, capacity
         dev = torch.device(device)
         self.batch, self.num_kv_heads, self.capacity = B, H, C
-        self.k_codes = torch.zeros((B, H, C, 32), dtype=torch.uint8, device=dev)
-        self.k_sz = torch.zeros((B, H, C // GROUP, HEAD_DIM, 2), dtype=torch.int16, device=dev)
-        self.k_norm = torch.zeros((B, H, C), dtype=torch.int16, device=dev)
-        self.v_codes = torch.zeros((B, H, C // GROUP, HEAD_DIM, 32), dtype=torch.uint8, device=dev)
-        self.v_sz = torch.zeros((B, H, C, 2), dtype=torch.int16, device=dev)
+        self.blocks = torch.zeros((B, H, C // GROUP, BLOCK_BYTES), dtype=torch.uint8, device=dev)
         self.k_tail = torch.zeros((B, H, GROUP, HEAD_DIM), dtype=torch.bfloat16, device=dev)
         self.v_tail = torch.zeros((B, H, GROUP, HEAD_DIM), dtype=torch.bfloat16, device=dev)
 
+    def _part(self, off: int, nbytes: int, dtype, shape):
+        v = self.blocks[..., off:off + nbytes]
+        if dtype is not torch.uint8:
+            v = v.view(dtype)
+        return v.view(*self.blocks.shape[:3], *shape)
+
+    @property
+    def k_codes(self) -> torch.Tensor:
+        return self._part(BLOCK_K_CODES, 4096, torch.uint8, (GROUP, 32))
+
+    @property
+    def v_codes(self) -> torch.Tensor:
+        return self._part(BLOCK_V_CODES, 4096, torch.uint8, (HEAD_DIM, 32))
+
+    @property
+    def k_sz(self) -> torch.Tensor:
+        return self._part(BLOCK_K_SZ, 512, torch.int16, (HEAD_DIM, 2))
+
+    @property
+    def v_sz(self) -> torch.Tensor:
+        return self._part(BLOCK_V_SZ, 512, torch.int16, (GROUP, 2))
+
+    @property
+    def k_norm(self) -> torch.Tensor:
+        return self._part(BLOCK_K_NORM, 256, torch.int16, (GROUP,))
+
     def desc(self) -> KVCacheDesc:
+        blocks = _ptr(self.blocks, torch.uint8, "blocks")
+        if blocks % 256:
+            raise ValueError("blocks must be 256-byte aligned")
         return KVCacheDesc(
-            self.batch, self.num_kv_heads, HEAD_DIM, GROUP, self.capacity,
-            _ptr(self.k_codes, torch.uint8, "k_codes"), _ptr(self.k_sz, torch.int16, "k_sz"),
-            _ptr(self.k_norm, torch.int16, "k_norm"), _ptr(self.v_codes, torch.uint8, "v_codes"),
-            _ptr(self.v_sz, torch.int16, "v_sz"), _ptr(self.k_tail, torch.bfloat16, "k_tail"),
-            _ptr(self.v_tail, torch.bfloat16, "v_tail"))
+            self.batch, self.num_kv_heads, HEAD_DIM, GROUP, self.capacity, blocks,
+            _ptr(self.k_tail, torch.bfloat16, "k_tail"), _ptr(self.v_tail, torch.bfloat16, "v_tail"))
 
     def nbytes_packed(self) -> int:
         """Bytes of the packed representation (codes, scales, zero-points, norms)."""
-        return sum(t.numel() * t.element_size() for t in
-                   (self.k_codes, self.k_sz, self.k_norm, self.v_codes, self.v_sz))
+        return self.blocks.numel()
 
 
 def quantize_kv(cache: PackedCache, k_src: torch.Tensor, v_src: torch.Tensor,

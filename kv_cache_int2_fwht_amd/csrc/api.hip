@@ -108,12 +108,9 @@ oscar_status check_cache(const char* fn, const oscar_kv_cache* c) {
   if (c->batch > 65535 || c->num_kv_heads > 65535) return fail(OSCAR_EINVAL, "%s: batch and num_kv_heads must be <= 65535", fn);
   if (c->capacity <= 0 || c->capacity % OSCAR_GROUP != 0)
     return fail(OSCAR_EINVAL, "%s: capacity must be a positive multiple of 128 (got %d)", fn, c->capacity);
-  const void* ptrs[5] = {c->k_codes, c->k_sz, c->k_norm, c->v_codes, c->v_sz};
-  const char* names[5] = {"k_codes", "k_sz", "k_norm", "v_codes", "v_sz"};
-  for (int i = 0; i < 5; ++i) {
-    if (!ptrs[i]) return fail(OSCAR_EINVAL, "%s: cache->%s is NULL", fn, names[i]);
-    if (!aligned16(ptrs[i])) return fail(OSCAR_EINVAL, "%s: cache->%s is not 16-byte aligned", fn, names[i]);
-  }
+  if (!c->blocks) return fail(OSCAR_EINVAL, "%s: cache->blocks is NULL", fn);
+  if ((reinterpret_cast<uintptr_t>(c->blocks) & 255u) != 0)
+    return fail(OSCAR_EINVAL, "%s: cache->blocks is not 256-byte aligned", fn);
   if ((c->k_tail && !aligned16(c->k_tail)) || (c->v_tail && !aligned16(c->v_tail)))
     return fail(OSCAR_EINVAL, "%s: tail buffers must be 16-byte aligned", fn);
   return OSCAR_OK;
@@ -162,11 +159,7 @@ oscar_status oscar_quantize_kv(const oscar_kv_cache* cache, const uint16_t* k_sr
   if (max_groups == 0) return ok();
   if ((st = check_device(fn)) != OSCAR_OK) return st;
   QuantizeArgs a;
-  a.k_codes = cache->k_codes;
-  a.k_sz = cache->k_sz;
-  a.k_norm = cache->k_norm;
-  a.v_codes = cache->v_codes;
-  a.v_sz = cache->v_sz;
+  a.blocks = cache->blocks;
   a.k_src = k_src;
   a.v_src = v_src;
   a.sb = src_stride_b;
@@ -212,11 +205,7 @@ oscar_status decode_int2_splits(const char* fn, const oscar_kv_cache* cache, con
   if ((st = check_device(fn)) != OSCAR_OK) return st;
   const SplitPlan p = plan_int2(cache->batch, cache->num_kv_heads, max_tokens);
   DecodeInt2Args a;
-  a.k_codes = cache->k_codes;
-  a.k_sz = cache->k_sz;
-  a.k_norm = cache->k_norm;
-  a.v_codes = cache->v_codes;
-  a.v_sz = cache->v_sz;
+  a.blocks = cache->blocks;
   a.k_tail = cache->k_tail;
   a.v_tail = cache->v_tail;
   a.n_quant = n_quant;

@@ -78,6 +78,9 @@ __device__ void load_and_rotate_q(const uint16_t* q, float scale, float (*dst_ra
   rotate_q<G, kRows>(fetch_q<G, kRows>(q), scale, dst_raw, dst_rot);
 }
 
+// Hardware 2^x (about 1 ulp; 2^-inf = 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Softmax states of G heads from kSlots producers (waves, plus extra slots
 // such as a bf16-tail state) of one workgroup.  A producer that saw no
 // token leaves m = -inf, l = 0, acc = 0.
@@ -112,15 +115,21 @@ __device__ void write_partial(MergeSmem<G, kSlots>& sm, float* partials, size_t 
   for (int i = tid; i < G * kHeadDim; i += blockDim.x) {
     const int hh = i / kHeadDim;
     const int d = i % kHeadDim;
+    float m[kSlots];
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kSlots; ++w) M = fmaxf(M, sm.m[w][hh]);
-    float Lsum = 0.f, A = 0.f;
-#pragma unroll
     for (int w = 0; w < kSlots; ++w) {
-      const float f = (sm.m[w][hh] == -INFINITY) ? 0.f : exp2f(sm.m[w][hh] - M);
-      Lsum += sm.l[w][hh] * f;
-      A += sm.acc[w][hh][d] * f;
+      m[w] = sm.m[w][hh];
+      M = fmaxf(M, m[w]);
+    }
+    float Lsum = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kSlots; ++w) {
+        const float f = fast_exp2(m[w] - M);   // 0 for an empty slot (m = -inf)
+        Lsum = fmaf(sm.l[w][hh], f, Lsum);
+        A = fmaf(sm.acc[w][hh][d], f, A);
+      }
     }
     float* rec = partials + (partial_base + static_cast<size_t>(hh) * splits + split) * kPartialFloats;
     rec[4 + d] = A;

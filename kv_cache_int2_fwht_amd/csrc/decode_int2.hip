@@ -87,8 +87,6 @@ __device__ __forceinline__ int fixed_off(float y) { return static_cast<int>(y + 
 
 // 2^x for x <= 0 with the hardware exponential: results below 2^-126 flush
 // to zero (negligible weights in a softmax); 2^-inf = 0.
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 // Maximum over the 16 lanes of a DPP row of non-negative floats (compared as
 // their bit patterns, which order them).
 __device__ __forceinline__ float row_max16_nonneg(float x) {
@@ -129,17 +127,21 @@ struct GroupBytes {
   uint2 ksz[4];     // (s | z << 16) of channels 16w + 4b + u + {0, 1}
 };
 
-// A group's bytes in LDS, as one loader wave copies them with direct
-// global -> LDS loads (16 bytes per lane per instruction, one contiguous
-// kilobyte per wave instruction).  Compute waves read their lane's operands
-// from it (read_stage).
-constexpr int kStageK = 0;         // 4096 B: key code half rows (16 B), order given by k_slot
-constexpr int kStageV = 4096;      // 4096 B: value code rows, channel-major as in memory
-constexpr int kStageKsz = 8192;    // 512 B: (s, z) per channel
-constexpr int kStageVsz = 8704;    // 512 B: (vs, vz) per token
-constexpr int kStageNorm = 9216;   // 256 B: fp16 norms
-constexpr int kStageBytes = 9472;
+// A group's block in LDS, as a loader wave copies it with direct global ->
+// LDS loads (16 bytes per lane per instruction, one contiguous kilobyte per
+// wave instruction): the block's own layout, except that the key code rows
+// are permuted (k_slot).  Compute waves read their lane's operands from it
+// (read_stage).
+constexpr int kStageK = OSCAR_BLOCK_K_CODES;   // 4096 B: key code half rows (16 B), order given by k_slot
+constexpr int kStageV = OSCAR_BLOCK_V_CODES;   // 4096 B: value code rows, channel-major
+constexpr int kStageKsz = OSCAR_BLOCK_K_SZ;    // 512 B: (s, z) per channel
+constexpr int kStageVsz = OSCAR_BLOCK_V_SZ;    // 512 B: (vs, vz) per token
+constexpr int kStageNorm = OSCAR_BLOCK_K_NORM; // 256 B: fp16 norms
+constexpr int kStageBytes = OSCAR_BLOCK_BYTES;
 constexpr int kDmaPerGroup = 10;   // load instructions per group (the norms take one of them)
+static_assert(kStageV == 4096 && kStageKsz == 8192 && kStageVsz == kStageKsz + 512 && kStageNorm == 9216 &&
+                  kStageBytes == 9472,
+              "the copy below assumes this block layout");
 
 // LDS slot of half row hh of token t: the XOR with bit 4 of t makes the
 // 8-byte reads of a score tile hit every bank equally often.
@@ -158,22 +160,17 @@ __device__ __forceinline__ void lds_load16(const void* gptr, const uint8_t* lds)
 // The kDmaPerGroup loads that copy group g of a slice into a stage.
 __device__ __forceinline__ void dma_group(uint8_t* stage, const DecodeInt2Args& a, size_t slice, int groups_cap,
                                           int g, int lane) {
-  const size_t row0 = slice * a.capacity + static_cast<size_t>(g) * kGroup;   // first token row
-  const size_t grp = slice * groups_cap + g;
+  const uint8_t* blk = a.blocks + (slice * groups_cap + g) * static_cast<size_t>(kStageBytes);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int sl = 64 * j + lane;                       // stage slot this lane fills
     const int t = (sl >> 1) ^ ((sl >> 5) & 1);          // the inverse of k_slot
-    lds_load16(a.k_codes + (row0 + t) * 32 + 16 * (sl & 1), stage + kStageK + 1024 * j);
+    lds_load16(blk + kStageK + t * 32 + 16 * (sl & 1), stage + kStageK + 1024 * j);
   }
-  const uint8_t* vsrc = a.v_codes + grp * (kHeadDim * 32) + 16 * lane;
+  // value codes, then the key and value (s, z) pairs: 5 contiguous kilobytes
 #pragma unroll
-  for (int j = 0; j < 4; ++j) lds_load16(vsrc + 1024 * j, stage + kStageV + 1024 * j);
-  const uint8_t* szsrc = (lane < 32) ? reinterpret_cast<const uint8_t*>(a.k_sz) + grp * 512 + 16 * lane
-                                     : reinterpret_cast<const uint8_t*>(a.v_sz) + row0 * 4 + 16 * (lane - 32);
-  lds_load16(szsrc, stage + kStageKsz);
-  const uint8_t* nsrc = reinterpret_cast<const uint8_t*>(a.k_norm) + row0 * 2 + 16 * (lane & 15);
-  if (lane < 16) lds_load16(nsrc, stage + kStageNorm);
+  for (int j = 0; j < 5; ++j) lds_load16(blk + kStageV + 1024 * j + 16 * lane, stage + kStageV + 1024 * j);
+  if (lane < 16) lds_load16(blk + kStageNorm + 16 * lane, stage + kStageNorm);
 }
 
 // Wait until at most `rem` groups' copies of this wave are outstanding
@@ -316,7 +313,7 @@ struct Int2Cfg {
   static constexpr int kLoaders = 2;
   static constexpr int kCompute = kWaves - kLoaders;
   static constexpr int kThreads = kWaves * kWave;
-  static constexpr int kSlots = kWaves + 1;  // one merge slot per wave (the loaders' stay empty) + the bf16 tail
+  static constexpr int kSlots = kCompute + 1;  // one merge slot per compute wave + one for the bf16 tail
   static constexpr int kRing = 12;           // group stages in LDS (a multiple of kLoaders)
   static constexpr int kAhead = 2;           // groups each loader has in flight (kAhead * kDmaPerGroup <= 63)
   static_assert(kRing % kLoaders == 0, "a stage is always refilled by the same loader");
@@ -508,35 +505,60 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
   __shared__ Int2Smem<G> sm;
 
   const int groups_cap = a.capacity / kGroup;
-  int nq = a.n_quant[b];
-  int nt = a.n_tail[b];
-  nq = min(max(nq, 0) & ~(kGroup - 1), a.capacity);
-  nt = min(max(nt, 0), kGroup - 1);
-  if (a.k_tail == nullptr || a.v_tail == nullptr) nt = 0;
-  const int total = min(nq + nt, a.max_tokens);
   // Split s owns the groups s, s + S, s + 2S, ... (S = number of splits):
   // at any moment the workgroups of a head read neighbouring groups, which
   // spreads the traffic over all memory channels.
   const int S = a.splits;
-  const int n_groups = (total + kGroup - 1) / kGroup;
   const size_t slice = static_cast<size_t>(b) * a.num_kv_heads + h;
   const int qh0 = h * G;
 
-  const int g_qend = min(n_groups, nq / kGroup);   // quantized groups end here; a tail group may follow
-  // this split's quantized groups: index k is group split + k S
-  const int n_k = (g_qend > split) ? (g_qend - split + S - 1) / S : 0;
+  // Wave roles: waves 0 .. kLoaders-1 (started first) stream the cache,
+  // the others (compute wave cw = wave - kLoaders) compute.
+  const bool loader = wave < C::kLoaders;
+  const int cw = wave - C::kLoaders;
 
-  // Start-up: wave 0 requests the query first (the barrier orders the
-  // requests of the compute unit), then sets it up while the loader wave
-  // starts streaming the cache.
+  // Start-up.  Compute wave 0 requests the query; the loaders request their
+  // first groups right after the barrier, before anything waits for the
+  // sequence lengths: the first groups are chosen from the capacity alone
+  // (always inside the buffer) and are simply not used if the sequence turns
+  // out to be shorter.  (A wave issuing cache copies can stall on issue for
+  // a while, so no wave issues them before the barrier.)
   uint4 q_in[RB];
-  if (wave == 0) fetch_q_wave<G, RB>(a.q + (static_cast<size_t>(b) * a.num_q_heads + qh0) * kHeadDim, lane, q_in);
+  if (cw == 0) fetch_q_wave<G, RB>(a.q + (static_cast<size_t>(b) * a.num_q_heads + qh0) * kHeadDim, lane, q_in);
   if (tid < C::kRing) {
     sm.filled[tid] = 0;
     sm.emptied[tid] = 0;
   }
   if (tid == 0) sm.q_ready = 0;
   __syncthreads();
+
+  int issued = 0;   // groups this loader has requested, in order (its j-th is k = wave + j kLoaders)
+  if (loader) {
+    static_assert(C::kAhead * C::kLoaders <= C::kRing, "the first groups go to unused stages");
+#pragma unroll
+    for (int j = 0; j < C::kAhead; ++j) {
+      const int k = wave + j * C::kLoaders;
+      if (split + k * S >= groups_cap) break;
+      dma_group(sm.u.ring[k % C::kRing], a, slice, groups_cap, split + k * S, lane);
+      ++issued;
+    }
+  }
+
+  // The lengths, read with scalar loads and waited for with the scalar
+  // counter, so that the wait does not include the cache copies above.
+  int nq, nt;
+  asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=&s"(nq), "=&s"(nt)
+               : "s"(a.n_quant + b), "s"(a.n_tail + b)
+               : "memory");
+  nq = min(max(nq, 0) & ~(kGroup - 1), a.capacity);
+  nt = min(max(nt, 0), kGroup - 1);
+  if (a.k_tail == nullptr || a.v_tail == nullptr) nt = 0;
+  const int total = min(nq + nt, a.max_tokens);
+  const int n_groups = (total + kGroup - 1) / kGroup;
+  const int g_qend = min(n_groups, nq / kGroup);   // quantized groups end here; a tail group may follow
+  // this split's quantized groups: index k is group split + k S
+  const int n_k = (g_qend > split) ? (g_qend - split + S - 1) / S : 0;
 
   WaveRun<RB> st;
 #pragma unroll
@@ -548,41 +570,34 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
     for (int j = 0; j < 8; ++j) st.acc[rb][j] = 0.f;
   }
 
-  if (wave >= C::kCompute) {
+  if (loader) {
     // ---- loaders: stream the split's groups through the ring ----
-    // Loader i copies the groups k = i, i + kLoaders, ...; group k goes to
-    // stage k % kRing once its previous occupant (k - kRing, the same
-    // loader's) has been read into registers.  A group is published once
-    // its copies have reached LDS, which the wave's in-order vector-memory
-    // counter shows when only the loads of the loader's kAhead - 1 later
-    // groups are still outstanding.
-    const int li = wave - C::kCompute;
-    const int n_mine = (n_k > li) ? (n_k - li + C::kLoaders - 1) / C::kLoaders : 0;
+    // Loader i copies the groups k = i, i + kLoaders, ... with up to kAhead
+    // of them in flight; group k goes to stage k % kRing once its previous
+    // occupant (k - kRing, the same loader's) has been read into registers.
+    // A group is published once its copies have reached LDS, which the
+    // wave's in-order vector-memory counter shows when only the loads of
+    // later groups are outstanding.
+    const int n_mine = (n_k > wave) ? (n_k - wave + C::kLoaders - 1) / C::kLoaders : 0;
     for (int j = 0; j < n_mine; ++j) {
-      const int k = li + j * C::kLoaders;
-      const int s = k % C::kRing;
-      const int use = k / C::kRing;   // earlier occupants of the stage
-      while (__hip_atomic_load(&sm.emptied[s], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < use)
-        __builtin_amdgcn_s_sleep(1);
-      dma_group(sm.u.ring[s], a, slice, groups_cap, split + k * S, lane);
-      if (j >= C::kAhead - 1) {
-        // the counter wait is the release: the copies are in LDS before the
-        // flag store issues (a release store would wait for every load)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((C::kAhead - 1) * kDmaPerGroup) : "memory");
-        const int kp = k - (C::kAhead - 1) * C::kLoaders;
-        __hip_atomic_store(&sm.filled[kp % C::kRing], kp / C::kRing + 1, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_WORKGROUP);
+      for (; issued < min(j + C::kAhead, n_mine); ++issued) {
+        const int k = wave + issued * C::kLoaders;
+        const int s = k % C::kRing;
+        const int use = k / C::kRing;   // earlier occupants of the stage
+        while (__hip_atomic_load(&sm.emptied[s], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < use)
+          __builtin_amdgcn_s_sleep(1);
+        dma_group(sm.u.ring[s], a, slice, groups_cap, split + k * S, lane);
       }
+      // the counter wait is the release: the copies are in LDS before the
+      // flag store issues (a release store would wait for every load)
+      wait_groups_outstanding<C::kAhead - 1>(issued - 1 - j);
+      const int k = wave + j * C::kLoaders;
+      __hip_atomic_store(&sm.filled[k % C::kRing], k / C::kRing + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    // the last groups: each is published as soon as its own copies are done
-    for (int j = max(n_mine - (C::kAhead - 1), 0); j < n_mine; ++j) {
-      wait_groups_outstanding<C::kAhead - 2>(n_mine - 1 - j);
-      const int kp = li + j * C::kLoaders;
-      __hip_atomic_store(&sm.filled[kp % C::kRing], kp / C::kRing + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
+    // first groups requested for nothing must land before the ring is reused
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else {
-    if (wave == 0) {
+    if (cw == 0) {
       rotate_q_wave<RB>(q_in, a.sm_scale * kLog2e, sm.q_raw, sm.q_rot, lane);
       // every lane releases its own writes
       __hip_atomic_store(&sm.q_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -600,11 +615,11 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
     // weight divisors of the bit pairs u + c this lane's values occupy
     const float fac[2] = {kFac[2 * (n & 1)], kFac[2 * (n & 1) + 1]};
 
-    // ---- compute waves: wave w takes the groups k = w, w + W, w + 2W, ...
-    // (W compute waves); a fixed assignment keeps the summation order, and
-    // so the result, the same from run to run ----
+    // ---- compute waves: compute wave w takes the groups k = w, w + W,
+    // w + 2W, ... (W compute waves); a fixed assignment keeps the summation
+    // order, and so the result, the same from run to run ----
     GroupBytes cur;
-    for (int k = wave; k < n_k; k += C::kCompute) {
+    for (int k = cw; k < n_k; k += C::kCompute) {
       const int s = k % C::kRing;
       const int use = k / C::kRing;
       while (__hip_atomic_load(&sm.filled[s], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <= use)
@@ -615,17 +630,24 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
       __hip_atomic_store(&sm.emptied[s], use + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       const int g = split + k * S;
       float alpha[RB], inv_p[RB];
-      score_phase<G>(cur, g * kGroup, total, qv, fac, sm, st, wave, gl, n, alpha, inv_p);
-      value_phase<G>(cur, sm, st, wave, gl, n, alpha, inv_p);
+      score_phase<G>(cur, g * kGroup, total, qv, fac, sm, st, cw, gl, n, alpha, inv_p);
+      value_phase<G>(cur, sm, st, cw, gl, n, alpha, inv_p);
     }
   }
 
-  // ---- every wave's state -> its merge slot (the slots replace the ring) ----
+  // ---- every compute wave's state -> its merge slot, the bf16 tail (at
+  // most one partial group, after the quantized ones) -> the last slot; the
+  // slots replace the ring ----
   __syncthreads();
-  if (wave >= C::kCompute) {
-    clear_slot(sm.u.merge, wave);
-    if (wave == C::kCompute) clear_slot(sm.u.merge, C::kWaves);   // the tail slot stays empty unless a tail is seen
-  } else {
+  if (wave == 0) {
+    clear_slot(sm.u.merge, C::kCompute);   // the tail slot stays empty unless a tail is seen
+    const int g_tail = nq / kGroup;
+    if (nt > 0 && g_tail < n_groups && g_tail % S == split) {
+      const int n_tok = min(nt, total - g_tail * kGroup);
+      bf16_tokens_wave<G, C::kSlots>(a.k_tail + slice * kGroup * kHeadDim, a.v_tail + slice * kGroup * kHeadDim,
+                                     n_tok, sm.q_raw, sm.tail_p, sm.u.merge, C::kCompute);
+    }
+  } else if (!loader) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float l_tot = row_sum16(st.l[rb]);
@@ -633,22 +655,13 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
       const int hh = rb * 4 + gl;
       if (hh < G) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sm.u.merge.acc[wave][hh][16 * j + n] = st.acc[rb][j] + z_tot;
+        for (int j = 0; j < 8; ++j) sm.u.merge.acc[cw][hh][16 * j + n] = st.acc[rb][j] + z_tot;
         if (n == 0) {
-          sm.u.merge.m[wave][hh] = st.m[rb];
-          sm.u.merge.l[wave][hh] = l_tot;
+          sm.u.merge.m[cw][hh] = st.m[rb];
+          sm.u.merge.l[cw][hh] = l_tot;
         }
       }
     }
-  }
-  __syncthreads();
-
-  // ---- the bf16 tail (at most one partial group, after the quantized ones) ----
-  const int g_tail = nq / kGroup;
-  if (nt > 0 && g_tail < n_groups && g_tail % S == split && wave == 0) {
-    const int n_tok = min(nt, total - g_tail * kGroup);
-    bf16_tokens_wave<G, C::kSlots>(a.k_tail + slice * kGroup * kHeadDim, a.v_tail + slice * kGroup * kHeadDim,
-                                   n_tok, sm.q_raw, sm.tail_p, sm.u.merge, C::kWaves);
   }
 
   const size_t partial_base = (static_cast<size_t>(b) * a.num_q_heads + qh0) * a.splits;

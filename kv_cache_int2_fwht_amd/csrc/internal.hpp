@@ -28,11 +28,7 @@ constexpr int kPartialFloats = 132;
 size_t partial_bytes(int32_t batch, int32_t num_q_heads, int32_t splits);
 
 struct QuantizeArgs {
-  uint8_t* k_codes;
-  uint16_t* k_sz;
-  uint16_t* k_norm;
-  uint8_t* v_codes;
-  uint16_t* v_sz;
+  uint8_t* blocks;
   const uint16_t* k_src;
   const uint16_t* v_src;
   int64_t sb, sh, st;
@@ -43,11 +39,7 @@ struct QuantizeArgs {
 };
 
 struct DecodeInt2Args {
-  const uint8_t* k_codes;
-  const uint16_t* k_sz;
-  const uint16_t* k_norm;
-  const uint8_t* v_codes;
-  const uint16_t* v_sz;
+  const uint8_t* blocks;
   const uint16_t* k_tail;
   const uint16_t* v_tail;
   const int32_t* n_quant;

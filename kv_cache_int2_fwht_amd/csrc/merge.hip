@@ -46,18 +46,25 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(const float
         v[k] = make_float2(0.f, 0.f);
       }
     }
+    // the batch's maximum first, so that its weights are independent
+    float Mb = ml[0].x;
+#pragma unroll
+    for (int k = 1; k < kMergeUnroll; ++k) Mb = fmaxf(Mb, ml[k].x);
+    const float M_new = fmaxf(M, Mb);
+    if (M_new == -INFINITY) continue;         // nothing seen yet (uniform over the wave)
+    const float r = fast_exp2(M - M_new);     // 0 while M was -inf
+    float Lb = 0.f, b0 = 0.f, b1 = 0.f;
 #pragma unroll
     for (int k = 0; k < kMergeUnroll; ++k) {
-      const float ms = ml[k].x;
-      if (ms == -INFINITY) continue;          // empty split (uniform over the wave)
-      const float M_new = fmaxf(M, ms);
-      const float r = (M == -INFINITY) ? 0.f : exp2f(M - M_new);
-      const float w = exp2f(ms - M_new);
-      L = fmaf(L, r, ml[k].y * w);
-      a0 = fmaf(a0, r, v[k].x * w);
-      a1 = fmaf(a1, r, v[k].y * w);
-      M = M_new;
+      const float w = fast_exp2(ml[k].x - M_new);   // 0 for an empty split
+      Lb = fmaf(ml[k].y, w, Lb);
+      b0 = fmaf(v[k].x, w, b0);
+      b1 = fmaf(v[k].y, w, b1);
     }
+    L = fmaf(L, r, Lb);
+    a0 = fmaf(a0, r, b0);
+    a1 = fmaf(a1, r, b1);
+    M = M_new;
   }
   if (lane == 0) {
     sm_m[wave] = M;
@@ -73,8 +80,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(const float
     if (Mt != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kMergeWaves; ++w) {
-        if (sm_m[w] == -INFINITY) continue;
-        const float f = exp2f(sm_m[w] - Mt);
+        const float f = fast_exp2(sm_m[w] - Mt);   // 0 for a wave that saw no split
         Lt = fmaf(sm_l[w], f, Lt);
         r0 = fmaf(sm_acc[w][lane].x, f, r0);
         r1 = fmaf(sm_acc[w][lane].y, f, r1);

@@ -102,8 +102,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const size_t slice = static_cast<size_t>(b) * a.num_kv_heads + h;
-  const size_t tok0 = slice * a.capacity + static_cast<size_t>(dst) * kGroup;
-  const size_t grp = slice * groups_cap + dst;
+  uint8_t* const blk = a.blocks + (slice * groups_cap + dst) * OSCAR_BLOCK_BYTES;   // this group's block
   const uint16_t* ksrc = a.k_src + b * a.sb + h * a.sh + static_cast<int64_t>(j) * kGroup * a.st;
   const uint16_t* vsrc = a.v_src + b * a.sb + h * a.sh + static_cast<int64_t>(j) * kGroup * a.st;
 
@@ -131,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
     const double n16 = f16_bits_to_f64(n16_bits);
     const double inv = (n16 > 0.0) ? 1.0 / (n16 * kSqrt128) : 0.0;
     if (L == 0) {
-      a.k_norm[tok0 + t] = n16_bits;
+      reinterpret_cast<uint16_t*>(blk + OSCAR_BLOCK_K_NORM)[t] = n16_bits;
       sm.inv_n[t] = inv;
     }
     // per-channel min / max over the four token slots of each 16-lane row
@@ -183,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
       if (cb == 0) {
         const uint16_t s_bits = f64_to_f16_bits_rne_sat((static_cast<double>(hi) - static_cast<double>(lo)) / 3.0);
         const uint16_t z_bits = f64_to_f16_bits_rne_sat(static_cast<double>(lo));
-        reinterpret_cast<uint32_t*>(a.v_sz)[tok0 + t] =
+        reinterpret_cast<uint32_t*>(blk + OSCAR_BLOCK_V_SZ)[t] =
             static_cast<uint32_t>(s_bits) | (static_cast<uint32_t>(z_bits) << 16);
         const double s16 = f16_bits_to_f64(s_bits);
         sm.vz[t] = f16_bits_to_f64(z_bits);
@@ -204,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
     }
     const uint16_t s_bits = f64_to_f16_bits_rne_sat((hi - lo) / 3.0);
     const uint16_t z_bits = f64_to_f16_bits_rne_sat(lo);
-    reinterpret_cast<uint32_t*>(a.k_sz)[grp * kHeadDim + tid] =
+    reinterpret_cast<uint32_t*>(blk + OSCAR_BLOCK_K_SZ)[tid] =
         static_cast<uint32_t>(s_bits) | (static_cast<uint32_t>(z_bits) << 16);
     const double s16 = f16_bits_to_f64(s_bits);
     sm.zs[tid] = f16_bits_to_f64(z_bits);
@@ -229,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
       }
       words[wd] = acc;
     }
-    *reinterpret_cast<uint4*>(a.v_codes + (grp * kHeadDim + d) * 32 + 16 * half) =
+    *reinterpret_cast<uint4*>(blk + OSCAR_BLOCK_V_CODES + d * 32 + 16 * half) =
         make_uint4(words[0], words[1], words[2], words[3]);
   }
   __syncthreads();
@@ -248,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
       w0 |= code_from(x[i] * inv, sm.zs[c0], sm.ss[c0], sm.inv_s[c0]) << (2 * i);
       w1 |= code_from(x[16 + i] * inv, sm.zs[c1], sm.ss[c1], sm.inv_s[c1]) << (2 * i);
     }
-    *reinterpret_cast<uint2*>(a.k_codes + (tok0 + t) * 32 + 8 * L) = make_uint2(w0, w1);
+    *reinterpret_cast<uint2*>(blk + OSCAR_BLOCK_K_CODES + t * 32 + 8 * L) = make_uint2(w0, w1);
   }
 }
 

@@ -31,16 +31,25 @@ def bits_to_dev_bf16(bits: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
 
 
+def token_rows(field: torch.Tensor, b: int, h: int, g0: int, ng: int) -> np.ndarray:
+    """Rows of a per-token cache field ([B, H, G, 128, ...] view) for groups
+    g0 .. g0+ng-1 of slice (b, h), with the group dimension folded into the
+    token dimension, as a host array."""
+    x = field[b, h, g0:g0 + ng].cpu().numpy()
+    return x.reshape(ng * x.shape[1], *x.shape[2:])
+
+
 def upload_slice(cache, b: int, h: int, s: "oracle.OracleSlice"):
     """Copy one oracle slice (packed bytes + bf16 tail) into a PackedCache."""
     n = s.n_quant
     dev = cache.k_codes.device
     if n:
-        cache.k_codes[b, h, :n] = torch.from_numpy(s.k_codes).to(dev)
-        cache.k_norm[b, h, :n] = torch.from_numpy(s.k_norm.view(np.int16)).to(dev)
-        cache.v_sz[b, h, :n] = torch.from_numpy(s.v_sz.view(np.int16)).to(dev)
-        cache.k_sz[b, h, :n // 128] = torch.from_numpy(s.k_sz.view(np.int16)).to(dev)
-        cache.v_codes[b, h, :n // 128] = torch.from_numpy(s.v_codes).to(dev)
+        ng = n // 128
+        cache.k_codes[b, h, :ng] = torch.from_numpy(s.k_codes.reshape(ng, 128, 32)).to(dev)
+        cache.k_norm[b, h, :ng] = torch.from_numpy(s.k_norm.view(np.int16).reshape(ng, 128)).to(dev)
+        cache.v_sz[b, h, :ng] = torch.from_numpy(s.v_sz.view(np.int16).reshape(ng, 128, 2)).to(dev)
+        cache.k_sz[b, h, :ng] = torch.from_numpy(s.k_sz.view(np.int16)).to(dev)
+        cache.v_codes[b, h, :ng] = torch.from_numpy(s.v_codes).to(dev)
     nt = s.k_tail.shape[0]
     if nt:
         from synthetic import f32_to_bf16_bits
@@ -84,13 +93,12 @@ def check_quantized_slice(cache, b: int, h: int, ref: "oracle.OracleSlice", g0: 
     slice quantized with keep_intermediates=True over the same tokens.
     Returns a dict of counts (exact-bit matches included)."""
     ng = ref.n_quant // 128 if ng is None else ng
-    t0, t1 = g0 * 128, (g0 + ng) * 128
     kq, vq = ref.kq, ref.vq
-    gk = cache.k_codes[b, h, t0:t1].cpu().numpy()
-    gn = cache.k_norm[b, h, t0:t1].cpu().numpy().view(np.uint16)
+    gk = token_rows(cache.k_codes, b, h, g0, ng)
+    gn = token_rows(cache.k_norm, b, h, g0, ng).view(np.uint16)
     gks = cache.k_sz[b, h, g0:g0 + ng].cpu().numpy().view(np.uint16)
     gv = cache.v_codes[b, h, g0:g0 + ng].cpu().numpy()
-    gvs = cache.v_sz[b, h, t0:t1].cpu().numpy().view(np.uint16)
+    gvs = token_rows(cache.v_sz, b, h, g0, ng).view(np.uint16)
 
     assert fp16_param_ok(gn, kq["n"]).all(), "key norms outside tolerance"
     s_pre, z_pre = kq["s_pre"], kq["z_pre"]

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert ob.abi_version() == 1
+    assert ob.abi_version() == 2
     assert ob.status_string(0) == "ok"
     assert ob.status_string(3) == "workspace too small"
     assert ob.status_string(99) == "unknown status"
@@ -69,8 +69,7 @@ needs_no_gpu = pytest.mark.skipif(not _no_gpu(), reason="placeholder pointers ar
 
 def _desc(**kw):
     d = dict(batch=1, num_kv_heads=8, head_dim=128, group=128, capacity=1024,
-             k_codes=0x10000, k_sz=0x20000, k_norm=0x30000, v_codes=0x40000, v_sz=0x50000,
-             k_tail=0x60000, v_tail=0x70000)
+             blocks=0x10000, k_tail=0x60000, v_tail=0x70000)
     d.update(kw)
     return ob.KVCacheDesc(*[d[f] for f, _ in ob.KVCacheDesc._fields_])
 
@@ -89,8 +88,10 @@ def test_decode_validation_errors():
     assert _decode(_desc(head_dim=64)) == ob.OSCAR_EUNSUPPORTED
     assert _decode(_desc(group=64)) == ob.OSCAR_EUNSUPPORTED
     assert _decode(_desc(capacity=1000)) == ob.OSCAR_EINVAL
-    assert _decode(_desc(k_codes=0)) == ob.OSCAR_EINVAL
-    assert _decode(_desc(v_sz=0x50008)) == ob.OSCAR_EINVAL          # misaligned
+    assert _decode(_desc(blocks=0)) == ob.OSCAR_EINVAL
+    assert _decode(_desc(blocks=0x10080)) == ob.OSCAR_EINVAL        # blocks not 256-byte aligned
+    assert b"256-byte" in L.oscar_last_error()
+    assert _decode(_desc(k_tail=0x60008)) == ob.OSCAR_EINVAL        # tail not 16-byte aligned
     assert _decode(_desc(), hq=30) == ob.OSCAR_EUNSUPPORTED           # not a multiple of 8 KV heads
     assert _decode(_desc(), hq=24) == ob.OSCAR_EUNSUPPORTED           # 3 query heads per KV head
     assert _decode(_desc(), max_tokens=-1) == ob.OSCAR_EINVAL

@@ -13,7 +13,7 @@ from tests.helpers import bits_to_dev_bf16
 pytestmark = pytest.mark.gpu
 
 SM = 1.0 / np.sqrt(128.0)
-STATE = ("k_codes", "k_sz", "k_norm", "v_codes", "v_sz", "k_tail", "v_tail")
+STATE = ("blocks", "k_tail", "v_tail")
 
 
 def _say(msg):

@@ -21,7 +21,7 @@ import torch
 
 import oracle
 import synthetic as syn
-from tests.helpers import assert_out_close, bits_to_dev_bf16, check_quantized_slice
+from tests.helpers import assert_out_close, bits_to_dev_bf16, check_quantized_slice, token_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -42,13 +42,12 @@ def _i32(vals):
 
 def _assert_bytes_equal(cache, b, h, ref, g0=0):
     """The GPU's packed bytes of slice (b, h) from group g0 on equal the oracle's."""
-    n = ref.n_quant
-    t0 = g0 * 128
-    assert np.array_equal(cache.k_codes[b, h, t0:t0 + n].cpu().numpy(), ref.k_codes)
-    assert np.array_equal(cache.k_norm[b, h, t0:t0 + n].cpu().numpy().view(np.uint16), ref.k_norm)
-    assert np.array_equal(cache.v_sz[b, h, t0:t0 + n].cpu().numpy().view(np.uint16), ref.v_sz)
-    assert np.array_equal(cache.k_sz[b, h, g0:g0 + n // 128].cpu().numpy().view(np.uint16), ref.k_sz)
-    assert np.array_equal(cache.v_codes[b, h, g0:g0 + n // 128].cpu().numpy(), ref.v_codes)
+    ng = ref.n_quant // 128
+    assert np.array_equal(token_rows(cache.k_codes, b, h, g0, ng), ref.k_codes)
+    assert np.array_equal(token_rows(cache.k_norm, b, h, g0, ng).view(np.uint16), ref.k_norm)
+    assert np.array_equal(token_rows(cache.v_sz, b, h, g0, ng).view(np.uint16), ref.v_sz)
+    assert np.array_equal(cache.k_sz[b, h, g0:g0 + ng].cpu().numpy().view(np.uint16), ref.k_sz)
+    assert np.array_equal(cache.v_codes[b, h, g0:g0 + ng].cpu().numpy(), ref.v_codes)
 
 
 def test_32k_group_append_over_128_steps(gpu_lib):
@@ -183,8 +182,7 @@ def test_batch8_jittered_lengths_sampled_slices(gpu_lib):
             v_dev[0, h, :n] = vd[:n]
         sub = ob.PackedCache(1, H, cap)
         ob.quantize_kv(sub, k_dev, v_dev, _i32([0]), _i32([nqs[b] // 128]), nqs[b] // 128)
-        for name in ("k_codes", "k_sz", "k_norm", "v_codes", "v_sz"):
-            getattr(cache, name)[b].copy_(getattr(sub, name)[0])
+        cache.blocks[b].copy_(sub.blocks[0])
         nt = lens[b] - nqs[b]
         cache.k_tail[b, :, :nt] = k_dev[0, :, nqs[b]:lens[b]]
         cache.v_tail[b, :, :nt] = v_dev[0, :, nqs[b]:lens[b]]

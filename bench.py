@@ -263,8 +263,8 @@ def main():
         ob.quantize_kv(cache, k_src, v_src, zeros, ngroups, T // 128)
 
     def timed_each(fn, n):
-        """Mean and median duration (us) of n calls, each bracketed by its own
-        pair of events on the launch stream."""
+        """p10, median and p90 duration (us) of n calls, each bracketed by its
+        own pair of events on the launch stream."""
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
         torch.cuda.synchronize()
         for i in range(n):
@@ -273,7 +273,7 @@ def main():
             ev[i][1].record(stream)
         torch.cuda.synchronize()
         d = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
-        return sum(d) / n, d[n // 2]
+        return d[n // 10], d[n // 2], d[(9 * n) // 10]
 
     def timed(fn, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -324,7 +324,12 @@ def main():
 
     for i in range(args.warmup):
         int2_kernel(i)
-    kern_us, kern_med_us = timed_each(int2_kernel, args.steps)
+    torch.cuda.synchronize()
+    # mean launch duration over the timed region (back-to-back launches,
+    # events at its two ends), and for reference the median of launches
+    # bracketed one by one (which adds each launch's own start-up)
+    kern_us = timed(int2_kernel, args.steps)
+    kern_p10, kern_med_us, kern_p90 = timed_each(int2_kernel, args.steps)
     # the same steps replayed from a HIP graph (no per-call host cost)
     int2_graph_us = graph_step_us([lambda c=c: ob.decode_attn(c, nq, nt, T, q, sm, out, ws) for c in caches],
                                   max(2, args.steps // len(caches)))
@@ -371,7 +376,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(kern_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kern_achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_int2_kernel<4>", "algorithmic_bytes_per_launch": int2_bytes,
-                     "kernel_us_mean": round(kern_us, 3), "kernel_us_median": round(kern_med_us, 3)},
+                     "kernel_us_mean": round(kern_us, 3), "kernel_us_isolated_p10_p50_p90": [round(kern_p10, 3), round(kern_med_us, 3), round(kern_p90, 3)]},
         "bf16_reference": {"us_per_step": round(bf16_us, 3),
                            "achieved_GBs": round(bf16_bytes / (bf16_us * 1e-6) / 1e9, 2),
                            "algorithmic_bytes_per_launch": bf16_bytes},

@@ -104,14 +104,15 @@ __device__ void clear_slot(MergeSmem<G, kSlots>& sm, int slot) {
 
 // Merge the slots and write this split's partial records
 // partials[(partial_base + hh * splits + split) * 132] = (m, l, -, -, acc[128]).
-// Must be reached by all threads of the block after the slots are written.
+// Must be reached by all threads of the block after the slots are written
+// (with a barrier first unless the caller has just passed one: kSync).
 // The records of all splits are merged by merge_splits_kernel, launched
 // after the decode kernel on the same stream.
-template <int G, int kSlots>
+template <int G, int kSlots, bool kSync = true>
 __device__ void write_partial(MergeSmem<G, kSlots>& sm, float* partials, size_t partial_base, int split,
                               int splits) {
   const int tid = threadIdx.x;
-  __syncthreads();
+  if (kSync) __syncthreads();
   for (int i = tid; i < G * kHeadDim; i += blockDim.x) {
     const int hh = i / kHeadDim;
     const int d = i % kHeadDim;

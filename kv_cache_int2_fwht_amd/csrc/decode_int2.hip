@@ -314,7 +314,8 @@ struct Int2Cfg {
   static constexpr int kCompute = kWaves - kLoaders;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kSlots = kCompute + 1;  // one merge slot per compute wave + one for the bf16 tail
-  static constexpr int kRing = 12;           // group stages in LDS (a multiple of kLoaders)
+  static constexpr int kRing = (kRB == 1) ? 10 : 8;   // group stages in LDS (a multiple of kLoaders)
+  static_assert(kWaves % 4 == 0 && kLoaders < 4, "compute waves on every SIMD");
   static constexpr int kAhead = 2;           // groups each loader has in flight (kAhead * kDmaPerGroup <= 63)
   static_assert(kRing % kLoaders == 0, "a stage is always refilled by the same loader");
   static_assert(kAhead * kDmaPerGroup <= 63, "vector-memory counter limit");
@@ -329,11 +330,8 @@ struct Int2Smem {
   // [half][lane group][row][16 bytes] (the scores' q digits, then the
   // values' p digits)
   uint8_t a_op[Int2Cfg<G>::kCompute][Int2Cfg<G>::kRB][2 * 4 * kOpBlock];
-  // the ring of group stages; once every group is computed, the merge slots
-  union {
-    uint8_t ring[Int2Cfg<G>::kRing][kStageBytes];
-    MergeSmem<G, Int2Cfg<G>::kSlots> merge;
-  } u;
+  uint8_t ring[Int2Cfg<G>::kRing][kStageBytes];      // group stages
+  MergeSmem<G, Int2Cfg<G>::kSlots> merge;              // final state of each compute wave, and of the bf16 tail
   int filled[Int2Cfg<G>::kRing];    // stage s holds group index k = s + kRing * (filled[s] - 1)
   int emptied[Int2Cfg<G>::kRing];   // times stage s has been read into registers
   int q_ready;                      // set by wave 0 once q_raw and q_rot are written
@@ -539,7 +537,7 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
     for (int j = 0; j < C::kAhead; ++j) {
       const int k = wave + j * C::kLoaders;
       if (split + k * S >= groups_cap) break;
-      dma_group(sm.u.ring[k % C::kRing], a, slice, groups_cap, split + k * S, lane);
+      dma_group(sm.ring[k % C::kRing], a, slice, groups_cap, split + k * S, lane);
       ++issued;
     }
   }
@@ -586,7 +584,7 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
         const int use = k / C::kRing;   // earlier occupants of the stage
         while (__hip_atomic_load(&sm.emptied[s], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < use)
           __builtin_amdgcn_s_sleep(1);
-        dma_group(sm.u.ring[s], a, slice, groups_cap, split + k * S, lane);
+        dma_group(sm.ring[s], a, slice, groups_cap, split + k * S, lane);
       }
       // the counter wait is the release: the copies are in LDS before the
       // flag store issues (a release store would wait for every load)
@@ -594,8 +592,20 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
       const int k = wave + j * C::kLoaders;
       __hip_atomic_store(&sm.filled[k % C::kRing], k / C::kRing + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    // first groups requested for nothing must land before the ring is reused
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // first groups requested for nothing included
+    if (wave == 0) {
+      // ---- the bf16 tail (at most one partial group, after the quantized
+      // ones) -> the last merge slot, while the compute waves still work ----
+      clear_slot(sm.merge, C::kCompute);   // stays empty unless a tail is seen
+      const int g_tail = nq / kGroup;
+      if (nt > 0 && g_tail < n_groups && g_tail % S == split) {
+        while (__hip_atomic_load(&sm.q_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+          __builtin_amdgcn_s_sleep(1);
+        const int n_tok = min(nt, total - g_tail * kGroup);
+        bf16_tokens_wave<G, C::kSlots>(a.k_tail + slice * kGroup * kHeadDim, a.v_tail + slice * kGroup * kHeadDim,
+                                       n_tok, sm.q_raw, sm.tail_p, sm.merge, C::kCompute);
+      }
+    }
   } else {
     if (cw == 0) {
       rotate_q_wave<RB>(q_in, a.sm_scale * kLog2e, sm.q_raw, sm.q_rot, lane);
@@ -615,16 +625,22 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
     // weight divisors of the bit pairs u + c this lane's values occupy
     const float fac[2] = {kFac[2 * (n & 1)], kFac[2 * (n & 1) + 1]};
 
-    // ---- compute waves: compute wave w takes the groups k = w, w + W,
-    // w + 2W, ... (W compute waves); a fixed assignment keeps the summation
-    // order, and so the result, the same from run to run ----
+    // ---- compute waves: group k goes to SIMD k % 4 (a workgroup's wave w
+    // runs on SIMD w % 4), and the SIMD's compute waves take its groups in
+    // turn, so that neighbouring groups, in particular the last ones to
+    // arrive, are computed on different SIMDs.  The assignment is fixed,
+    // which keeps the summation order, and so the result, the same from run
+    // to run ----
+    const int simd = wave % 4;
+    const int first_i = (simd < C::kLoaders) ? 1 : 0;                  // SIMD's first compute wave: simd + 4 first_i
+    const int n_simd = (C::kWaves - 1 - simd) / 4 + 1 - first_i;      // compute waves on this SIMD
     GroupBytes cur;
-    for (int k = cw; k < n_k; k += C::kCompute) {
+    for (int k = simd + 4 * (wave / 4 - first_i); k < n_k; k += 4 * n_simd) {
       const int s = k % C::kRing;
       const int use = k / C::kRing;
       while (__hip_atomic_load(&sm.filled[s], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <= use)
         __builtin_amdgcn_s_sleep(1);
-      read_stage(cur, sm.u.ring[s], lane);
+      read_stage(cur, sm.ring[s], lane);
       // the stage may be refilled once every lane's reads have returned
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __hip_atomic_store(&sm.emptied[s], use + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -635,19 +651,8 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
     }
   }
 
-  // ---- every compute wave's state -> its merge slot, the bf16 tail (at
-  // most one partial group, after the quantized ones) -> the last slot; the
-  // slots replace the ring ----
-  __syncthreads();
-  if (wave == 0) {
-    clear_slot(sm.u.merge, C::kCompute);   // the tail slot stays empty unless a tail is seen
-    const int g_tail = nq / kGroup;
-    if (nt > 0 && g_tail < n_groups && g_tail % S == split) {
-      const int n_tok = min(nt, total - g_tail * kGroup);
-      bf16_tokens_wave<G, C::kSlots>(a.k_tail + slice * kGroup * kHeadDim, a.v_tail + slice * kGroup * kHeadDim,
-                                     n_tok, sm.q_raw, sm.tail_p, sm.u.merge, C::kCompute);
-    }
-  } else if (!loader) {
+  if (!loader) {
+    // ---- this compute wave's state -> its merge slot ----
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float l_tot = row_sum16(st.l[rb]);
@@ -655,17 +660,18 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
       const int hh = rb * 4 + gl;
       if (hh < G) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sm.u.merge.acc[cw][hh][16 * j + n] = st.acc[rb][j] + z_tot;
+        for (int j = 0; j < 8; ++j) sm.merge.acc[cw][hh][16 * j + n] = st.acc[rb][j] + z_tot;
         if (n == 0) {
-          sm.u.merge.m[cw][hh] = st.m[rb];
-          sm.u.merge.l[cw][hh] = l_tot;
+          sm.merge.m[cw][hh] = st.m[rb];
+          sm.merge.l[cw][hh] = l_tot;
         }
       }
     }
   }
+  __syncthreads();
 
   const size_t partial_base = (static_cast<size_t>(b) * a.num_q_heads + qh0) * a.splits;
-  write_partial<G, C::kSlots>(sm.u.merge, a.partials, partial_base, split, a.splits);
+  write_partial<G, C::kSlots, false>(sm.merge, a.partials, partial_base, split, a.splits);
 }
 
 template <int G>

@@ -81,8 +81,18 @@ __device__ __forceinline__ void key_fwht(const uint16_t* row, int L, double (&x)
 }
 
 struct QuantSmem {
-  double red_min[16][kHeadDim];   // per-channel min / max of the scaled keys, one row per (wave, 16-lane row)
-  double red_max[16][kHeadDim];
+  // The group's block is assembled here and written out at the end in whole
+  // 16-byte pieces: its codes in `out_codes` (which reuses the key ranges'
+  // space once the key parameters are known), its (s, z) pairs and norms in
+  // `out_params`.
+  union alignas(16) {
+    struct {
+      double red_min[16][kHeadDim];   // per-channel min / max of the scaled keys, one row per (wave, 16-lane row)
+      double red_max[16][kHeadDim];
+    } r;
+    uint8_t out_codes[OSCAR_BLOCK_K_SZ];                        // key codes, then value codes
+  } u;
+  alignas(16) uint8_t out_params[OSCAR_BLOCK_BYTES - OSCAR_BLOCK_K_SZ];   // key (s, z), value (s, z), key norms
   double zs[kHeadDim], ss[kHeadDim], inv_s[kHeadDim];   // key (z16, s16, 1 / s16) per channel
   double inv_n[kGroup];                                  // 1 / (sqrt(128) n16) per token (0 if n16 = 0)
   double vz[kGroup], vs[kGroup], vinv[kGroup];           // value (z16, s16, 1 / s16) per token
@@ -130,7 +140,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
     const double n16 = f16_bits_to_f64(n16_bits);
     const double inv = (n16 > 0.0) ? 1.0 / (n16 * kSqrt128) : 0.0;
     if (L == 0) {
-      reinterpret_cast<uint16_t*>(blk + OSCAR_BLOCK_K_NORM)[t] = n16_bits;
+      reinterpret_cast<uint16_t*>(sm.out_params + (OSCAR_BLOCK_K_NORM - OSCAR_BLOCK_K_SZ))[t] = n16_bits;
       sm.inv_n[t] = inv;
     }
     // per-channel min / max over the four token slots of each 16-lane row
@@ -143,11 +153,11 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
       mx = fmax(mx, dpp_f64<kDppRowRor8>(mx));
       if ((lane & 15) < 4) {
         if (pass == 0) {
-          sm.red_min[row][32 * L + i] = mn;
-          sm.red_max[row][32 * L + i] = mx;
+          sm.u.r.red_min[row][32 * L + i] = mn;
+          sm.u.r.red_max[row][32 * L + i] = mx;
         } else {   // the same lane wrote these entries in the first pass
-          sm.red_min[row][32 * L + i] = fmin(sm.red_min[row][32 * L + i], mn);
-          sm.red_max[row][32 * L + i] = fmax(sm.red_max[row][32 * L + i], mx);
+          sm.u.r.red_min[row][32 * L + i] = fmin(sm.u.r.red_min[row][32 * L + i], mn);
+          sm.u.r.red_max[row][32 * L + i] = fmax(sm.u.r.red_max[row][32 * L + i], mx);
         }
       }
     }
@@ -182,7 +192,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
       if (cb == 0) {
         const uint16_t s_bits = f64_to_f16_bits_rne_sat((static_cast<double>(hi) - static_cast<double>(lo)) / 3.0);
         const uint16_t z_bits = f64_to_f16_bits_rne_sat(static_cast<double>(lo));
-        reinterpret_cast<uint32_t*>(blk + OSCAR_BLOCK_V_SZ)[t] =
+        reinterpret_cast<uint32_t*>(sm.out_params + (OSCAR_BLOCK_V_SZ - OSCAR_BLOCK_K_SZ))[t] =
             static_cast<uint32_t>(s_bits) | (static_cast<uint32_t>(z_bits) << 16);
         const double s16 = f16_bits_to_f64(s_bits);
         sm.vz[t] = f16_bits_to_f64(z_bits);
@@ -195,21 +205,23 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
 
   // ---------------- key parameters per channel ----------------
   if (tid < kHeadDim) {
-    double lo = sm.red_min[0][tid], hi = sm.red_max[0][tid];
+    double lo = sm.u.r.red_min[0][tid], hi = sm.u.r.red_max[0][tid];
 #pragma unroll
     for (int r = 1; r < 16; ++r) {
-      lo = fmin(lo, sm.red_min[r][tid]);
-      hi = fmax(hi, sm.red_max[r][tid]);
+      lo = fmin(lo, sm.u.r.red_min[r][tid]);
+      hi = fmax(hi, sm.u.r.red_max[r][tid]);
     }
     const uint16_t s_bits = f64_to_f16_bits_rne_sat((hi - lo) / 3.0);
     const uint16_t z_bits = f64_to_f16_bits_rne_sat(lo);
-    reinterpret_cast<uint32_t*>(blk + OSCAR_BLOCK_K_SZ)[tid] =
+    reinterpret_cast<uint32_t*>(sm.out_params)[tid] =
         static_cast<uint32_t>(s_bits) | (static_cast<uint32_t>(z_bits) << 16);
     const double s16 = f16_bits_to_f64(s_bits);
     sm.zs[tid] = f16_bits_to_f64(z_bits);
     sm.ss[tid] = s16;
     sm.inv_s[tid] = (s16 > 0.0) ? 1.0 / s16 : 0.0;
   }
+
+  __syncthreads();   // the key ranges are read: their space now takes the codes
 
   // ---------------- value codes: thread = (channel d, half of the group's tokens) ----------------
   {
@@ -228,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
       }
       words[wd] = acc;
     }
-    *reinterpret_cast<uint4*>(blk + OSCAR_BLOCK_V_CODES + d * 32 + 16 * half) =
+    *reinterpret_cast<uint4*>(sm.u.out_codes + OSCAR_BLOCK_V_CODES + d * 32 + 16 * half) =
         make_uint4(words[0], words[1], words[2], words[3]);
   }
   __syncthreads();
@@ -247,7 +259,16 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
       w0 |= code_from(x[i] * inv, sm.zs[c0], sm.ss[c0], sm.inv_s[c0]) << (2 * i);
       w1 |= code_from(x[16 + i] * inv, sm.zs[c1], sm.ss[c1], sm.inv_s[c1]) << (2 * i);
     }
-    *reinterpret_cast<uint2*>(blk + OSCAR_BLOCK_K_CODES + t * 32 + 8 * L) = make_uint2(w0, w1);
+    *reinterpret_cast<uint2*>(sm.u.out_codes + OSCAR_BLOCK_K_CODES + t * 32 + 8 * L) = make_uint2(w0, w1);
+  }
+  __syncthreads();
+
+  // ---------------- the block, written once with coalesced 16-byte stores ----------------
+  static_assert(OSCAR_BLOCK_K_CODES == 0 && OSCAR_BLOCK_V_CODES + 4096 == OSCAR_BLOCK_K_SZ, "codes first");
+  for (int i = tid; i < OSCAR_BLOCK_BYTES / 16; i += kThreads) {
+    const uint4 w = (i < OSCAR_BLOCK_K_SZ / 16) ? reinterpret_cast<const uint4*>(sm.u.out_codes)[i]
+                                                : reinterpret_cast<const uint4*>(sm.out_params)[i - OSCAR_BLOCK_K_SZ / 16];
+    reinterpret_cast<uint4*>(blk)[i] = w;
   }
 }
 

@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target seconds of oracle work")
     p.add_argument("--profile", choices=["none", "int2", "bf16", "quantize", "copy"], default="none",
                    help="run only one kernel (for rocprofv3 runs) and print its timing")
+    p.add_argument("--ablation", action="store_true",
+                   help="Token Norm Imbalance ablation on the 128K layer: attention-output error of each "
+                        "key-quantizer variant against the bf16 kernel on the same keys and values")
     p.add_argument("--sweep", action="store_true",
                    help="context sweep 8K..128K at batch 1 and 8: INT2 and bf16 decode steps, speed-up and "
                         "cache footprint (one JSON line per configuration instead of the benchmark line)")
@@ -217,6 +220,83 @@ def context_sweep(args):
             torch.cuda.empty_cache()
 
 
+def ablation(args):
+    """Attention-output error of the four key-quantizer variants (no rotation
+    and no scaling = plain per-channel INT2; rotation only; scaling only;
+    both = OScaR) on the 128K Llama-3.1-8B layer, against the bf16 kernel
+    over the same unquantized keys and values.  Values are quantized per
+    token in every variant, so the output error mixes both quantizers; the
+    key-only figures are the relative key error ||k - k^|| / ||k|| (mean,
+    99th percentile, and the attention-sink token 0) and the total-variation
+    distance between the attention weights over exact and dequantized keys
+    (mean and max over the 32 query heads), from the cache bytes dequantized
+    with torch (measurement only).  One JSON line per variant."""
+    import numpy as np
+    import torch
+    import synthetic as syn
+    from kv_cache_int2_fwht_amd import binding as ob
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = syn.workload(3)
+    B, H, Hq, T = w.batch, w.num_kv_heads, w.num_q_heads, w.lengths[0]
+    sm = 1.0 / np.sqrt(128.0)
+    k_src = torch.empty((B, H, T, 128), dtype=torch.bfloat16, device=dev)
+    v_src = torch.empty((B, H, T, 128), dtype=torch.bfloat16, device=dev)
+    for h in range(H):
+        k_src[0, h] = torch.from_numpy(syn.keys_slice(w, 0, h).view(np.int16)).to(dev).view(torch.bfloat16)
+        v_src[0, h] = torch.from_numpy(syn.values_slice(w, 0, h).view(np.int16)).to(dev).view(torch.bfloat16)
+    q = torch.from_numpy(syn.query(w, 0).view(np.int16)).to(dev).view(torch.bfloat16)[None].contiguous()
+    seq = torch.full((B,), T, dtype=torch.int32, device=dev)
+    ws = ob.alloc_workspace(B, H, Hq, T, device=dev)
+    ref = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    ob.decode_attn_bf16(k_src, v_src, seq, T, q, sm, ref, ws)
+    torch.cuda.synchronize()
+    ref_n = ref[0].double().norm(dim=-1)
+    variants = [("per_channel", ob.KEYS_UNROTATED | ob.KEYS_UNSCALED), ("rotation", ob.KEYS_UNSCALED),
+                ("scaling", ob.KEYS_UNROTATED), ("oscar", 0)]
+    # exact keys and logits (float32 keys, float64 softmax), for the key-only metrics
+    G = Hq // H
+    k32 = k_src[0].float()                                          # [H, T, 128]
+    q32 = q[0].float().view(H, G, 128)                              # query head j -> KV head j // G
+    p_ref = torch.softmax((sm * torch.bmm(q32, k32.transpose(1, 2).contiguous())).double(), dim=-1)
+    k_norm = k32.norm(dim=-1)                                       # [H, T]
+    n_i = torch.arange(128, device=dev, dtype=torch.int32)
+    hmat = torch.tensor(np.array([[(-1.0) ** bin(i & j).count("1") for j in range(128)] for i in range(128)])
+                        / np.sqrt(128.0), dtype=torch.float32, device=dev)   # Sylvester H, orthonormal, symmetric
+
+    def dequantized_keys(cache, rotated):
+        """k^ [H, T, 128] from the cache bytes, in k's basis (measurement only)."""
+        byt = cache.k_codes[0].to(torch.int32)                     # [H, Gr, 128 tok, 32 B]
+        codes = (byt[..., n_i // 4] >> (2 * (n_i % 4))) & 3          # [H, Gr, 128 tok, 128 ch]
+        sz = cache.k_sz[0].view(torch.float16).float()              # [H, Gr, 128 ch, 2]
+        n16 = cache.k_norm[0].view(torch.float16).float()           # [H, Gr, 128 tok]
+        y = n16[..., None] * (sz[:, :, None, :, 0] * codes.float() + sz[:, :, None, :, 1])
+        y = y.reshape(H, T, 128)
+        return y @ hmat if rotated else y                           # k = H^T y = H y
+
+    for name, flags in variants:
+        cache = ob.PackedCache(B, H, T, device=dev, flags=flags)
+        ob.quantize_kv(cache, k_src, v_src, torch.zeros(B, dtype=torch.int32, device=dev),
+                       torch.full((B,), T // 128, dtype=torch.int32, device=dev), T // 128)
+        out = torch.empty_like(ref)
+        ob.decode_attn(cache, seq, torch.zeros(B, dtype=torch.int32, device=dev), T, q, sm, out, ws)
+        torch.cuda.synchronize()
+        err = ((out[0].double() - ref[0].double()).norm(dim=-1) / ref_n).cpu().numpy()
+        k_hat = dequantized_keys(cache, not (flags & ob.KEYS_UNROTATED))
+        key_err = ((k32 - k_hat).norm(dim=-1) / k_norm)             # [H, T]
+        p_hat = torch.softmax((sm * torch.bmm(q32, k_hat.transpose(1, 2).contiguous())).double(), dim=-1)
+        tv = (0.5 * (p_ref - p_hat).abs().sum(dim=-1)).flatten().cpu().numpy()   # per query head
+        print(json.dumps({"ablation": name, "flags": flags, "context": T, "heads": Hq,
+                          "key_rel_err_mean": round(float(key_err.mean()), 5),
+                          "key_rel_err_p99": round(float(torch.quantile(key_err[:, 1:].flatten()[::16], 0.99)), 5),
+                          "key_rel_err_sink": round(float(key_err[:, 0].mean()), 5),
+                          "attn_tv_mean": round(float(tv.mean()), 5), "attn_tv_max": round(float(tv.max()), 5),
+                          "out_rel_err_mean": round(float(err.mean()), 6),
+                          "out_rel_err_max": round(float(err.max()), 6)}), flush=True)
+        del cache, k_hat, p_hat
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -227,6 +307,9 @@ def main():
 
     if args.sweep:
         context_sweep(args)
+        return
+    if args.ablation:
+        ablation(args)
         return
 
     import numpy as np

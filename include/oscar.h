@@ -90,12 +90,19 @@ typedef enum oscar_status {
 } oscar_status;
 
 /* Caller-owned packed cache (see the layout above). */
+/* oscar_kv_cache.flags: key-quantizer variants for the Token Norm Imbalance
+ * ablation (ai-papers.net OScaR summary, sections "TNIという根本課題の特定"
+ * and "OScaRの提案手法").  0 is the method: keys rotated, then scaled. */
+#define OSCAR_KEYS_UNROTATED 1   /* no Hadamard rotation: keys quantized as they are */
+#define OSCAR_KEYS_UNSCALED 2    /* no per-token L2 scaling: the stored norm is 1 */
+
 typedef struct oscar_kv_cache {
   int32_t batch;
   int32_t num_kv_heads;
   int32_t head_dim;        /* must be 128 */
   int32_t group;           /* must be 128 */
   int32_t capacity;        /* tokens per sequence; a positive multiple of 128 */
+  int32_t flags;           /* OSCAR_KEYS_* bits; the quantizer and the decode of a cache must agree */
   uint8_t* blocks;          /* [batch][num_kv_heads][capacity/128][OSCAR_BLOCK_BYTES] */
   const uint16_t* k_tail;  /* read by oscar_decode_attn only; may be NULL if no tail is ever used */
   const uint16_t* v_tail;

@@ -19,6 +19,8 @@ GROUP = 128
 # one group's block in the packed cache (byte offsets; include/oscar.h)
 BLOCK_K_CODES, BLOCK_V_CODES, BLOCK_K_SZ, BLOCK_V_SZ, BLOCK_K_NORM = 0, 4096, 8192, 8704, 9216
 BLOCK_BYTES = 9472
+# oscar_kv_cache.flags: key-quantizer variants (Token Norm Imbalance ablation)
+KEYS_UNROTATED, KEYS_UNSCALED = 1, 2
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "liboscar.so")
 _lib = None
@@ -40,6 +42,7 @@ class KVCacheDesc(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("group", ctypes.c_int32),
         ("capacity", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
         ("blocks", ctypes.c_void_p),
         ("k_tail", ctypes.c_void_p),
         ("v_tail", ctypes.c_void_p),
@@ -140,12 +143,13 @@ class PackedCache:
     k_tail / v_tail are bf16 [B,H,128,128].
     """
 
-    def __init__(self, batch: int, num_kv_heads: int, capacity: int, device="cuda"):
+    def __init__(self, batch: int, num_kv_heads: int, capacity: int, device="cuda", flags: int = 0):
         if capacity % GROUP:
             raise ValueError("capacity must be a multiple of 128")
         B, H, C = batch, num_kv_heads, capacity
         dev = torch.device(device)
         self.batch, self.num_kv_heads, self.capacity = B, H, C
+        self.flags = int(flags)   # KEYS_UNROTATED | KEYS_UNSCALED; 0 = OScaR
         self.blocks = torch.zeros((B, H, C // GROUP, BLOCK_BYTES), dtype=torch.uint8, device=dev)
         self.k_tail = torch.zeros((B, H, GROUP, HEAD_DIM), dtype=torch.bfloat16, device=dev)
         self.v_tail = torch.zeros((B, H, GROUP, HEAD_DIM), dtype=torch.bfloat16, device=dev)
@@ -181,7 +185,7 @@ class PackedCache:
         if blocks % 256:
             raise ValueError("blocks must be 256-byte aligned")
         return KVCacheDesc(
-            self.batch, self.num_kv_heads, HEAD_DIM, GROUP, self.capacity, blocks,
+            self.batch, self.num_kv_heads, HEAD_DIM, GROUP, self.capacity, self.flags, blocks,
             _ptr(self.k_tail, torch.bfloat16, "k_tail"), _ptr(self.v_tail, torch.bfloat16, "v_tail"))
 
     def nbytes_packed(self) -> int:

@@ -108,6 +108,8 @@ oscar_status check_cache(const char* fn, const oscar_kv_cache* c) {
   if (c->batch > 65535 || c->num_kv_heads > 65535) return fail(OSCAR_EINVAL, "%s: batch and num_kv_heads must be <= 65535", fn);
   if (c->capacity <= 0 || c->capacity % OSCAR_GROUP != 0)
     return fail(OSCAR_EINVAL, "%s: capacity must be a positive multiple of 128 (got %d)", fn, c->capacity);
+  if ((c->flags & ~(OSCAR_KEYS_UNROTATED | OSCAR_KEYS_UNSCALED)) != 0)
+    return fail(OSCAR_EINVAL, "%s: unknown bits in cache->flags (0x%x)", fn, static_cast<unsigned>(c->flags));
   if (!c->blocks) return fail(OSCAR_EINVAL, "%s: cache->blocks is NULL", fn);
   if ((reinterpret_cast<uintptr_t>(c->blocks) & 255u) != 0)
     return fail(OSCAR_EINVAL, "%s: cache->blocks is not 256-byte aligned", fn);
@@ -169,6 +171,7 @@ oscar_status oscar_quantize_kv(const oscar_kv_cache* cache, const uint16_t* k_sr
   a.num_groups = num_groups;
   a.num_kv_heads = cache->num_kv_heads;
   a.capacity = cache->capacity;
+  a.flags = cache->flags;
   return launched(launch_quantize(a, cache->batch, max_groups, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -215,6 +218,7 @@ oscar_status decode_int2_splits(const char* fn, const oscar_kv_cache* cache, con
   a.num_kv_heads = cache->num_kv_heads;
   a.num_q_heads = num_q_heads;
   a.capacity = cache->capacity;
+  a.flags = cache->flags;
   a.max_tokens = max_tokens;
   a.tokens_per_split = p.tokens_per_split;
   a.splits = p.splits;

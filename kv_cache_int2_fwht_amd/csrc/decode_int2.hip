@@ -614,14 +614,18 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
     }
     while (__hip_atomic_load(&sm.q_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
       __builtin_amdgcn_s_sleep(1);
-    // rotated query of this lane's head and channels 16w + 4b + u + c, per row block
+    // query of this lane's head and channels 16w + 4b + u + c, per row block:
+    // rotated like the keys (unrotated only for the ablation variant whose
+    // keys were quantized unrotated)
+    const float(*q_keys)[kHeadDim] = (a.flags & OSCAR_KEYS_UNROTATED) ? sm.q_raw : sm.q_rot;
     float qv[RB][2][4];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) qv[rb][c][b] = sm.q_rot[rb * 4 + gl][16 * (n >> 1) + 4 * b + 2 * (n & 1) + c];
+        for (int b = 0; b < 4; ++b)
+          qv[rb][c][b] = q_keys[rb * 4 + gl][16 * (n >> 1) + 4 * b + 2 * (n & 1) + c];
     // weight divisors of the bit pairs u + c this lane's values occupy
     const float fac[2] = {kFac[2 * (n & 1)], kFac[2 * (n & 1) + 1]};
 

@@ -36,6 +36,7 @@ struct QuantizeArgs {
   const int32_t* num_groups;
   int32_t num_kv_heads;
   int32_t capacity;
+  int32_t flags;   // OSCAR_KEYS_*
 };
 
 struct DecodeInt2Args {
@@ -53,6 +54,7 @@ struct DecodeInt2Args {
   int32_t tokens_per_split;
   int32_t splits;
   float sm_scale;
+  int32_t flags;   // OSCAR_KEYS_*
 };
 
 struct DecodeBf16Args {

@@ -45,7 +45,7 @@ __device__ __forceinline__ uint32_t code_from(double x, double z, double s, doub
 // Walsh-Hadamard transform Y = sqrt(128) H k in fp64 across the four lanes
 // L = 0..3 of a quad: channel bits 0..4 in-lane, bits 5 and 6 across the
 // quad (exact for bf16 inputs in practice).
-__device__ __forceinline__ void key_fwht(const uint16_t* row, int L, double (&x)[32]) {
+__device__ __forceinline__ void key_fwht(const uint16_t* row, int L, bool rotate, double (&x)[32]) {
   const uint4* src = reinterpret_cast<const uint4*>(row + 32 * L);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -57,6 +57,7 @@ __device__ __forceinline__ void key_fwht(const uint16_t* row, int L, double (&x)
       x[8 * q + 2 * e + 1] = static_cast<double>(bf16hi_to_f32(ws[e]));
     }
   }
+  if (!rotate) return;   // the rotation is switched off (ablation variants only)
 #pragma unroll
   for (int bit = 1; bit < 32; bit <<= 1) {
 #pragma unroll
@@ -111,6 +112,8 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
+  const bool rotate = (a.flags & OSCAR_KEYS_UNROTATED) == 0;
+  const bool scale = (a.flags & OSCAR_KEYS_UNSCALED) == 0;
   const size_t slice = static_cast<size_t>(b) * a.num_kv_heads + h;
   uint8_t* const blk = a.blocks + (slice * groups_cap + dst) * OSCAR_BLOCK_BYTES;   // this group's block
   const uint16_t* ksrc = a.k_src + b * a.sb + h * a.sh + static_cast<int64_t>(j) * kGroup * a.st;
@@ -128,17 +131,19 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
   for (int pass = 0; pass < 2; ++pass) {
     const int t = wave * 32 + pass * 16 + slot;
     double x[32];
-    key_fwht(ksrc + static_cast<int64_t>(t) * a.st, L, x);
-    // ||y||^2 = sum(Y^2) / 128 for the unnormalised transform Y = sqrt(128) y.
+    key_fwht(ksrc + static_cast<int64_t>(t) * a.st, L, rotate, x);
+    // ||y||^2 = sum(Y^2) / 128 for the unnormalised transform Y = sqrt(128) y
+    // (sum(k^2) when the rotation is off).
     double ssq = 0.0;
 #pragma unroll
     for (int i = 0; i < 32; ++i) ssq = fma(x[i], x[i], ssq);
     ssq += dpp_f64<kDppQuadXor1>(ssq);   // a + b == b + a: all four lanes agree
     ssq += dpp_f64<kDppQuadXor2>(ssq);
-    const double n = sqrt(ssq * (1.0 / 128.0));
-    const uint16_t n16_bits = f64_to_f16_bits_rne_sat(n);
+    const double n = rotate ? sqrt(ssq * (1.0 / 128.0)) : sqrt(ssq);
+    // without the scaling the stored norm is 1 and u = y
+    const uint16_t n16_bits = scale ? f64_to_f16_bits_rne_sat(n) : uint16_t{0x3C00};
     const double n16 = f16_bits_to_f64(n16_bits);
-    const double inv = (n16 > 0.0) ? 1.0 / (n16 * kSqrt128) : 0.0;
+    const double inv = (n16 > 0.0) ? 1.0 / (rotate ? n16 * kSqrt128 : n16) : 0.0;
     if (L == 0) {
       reinterpret_cast<uint16_t*>(sm.out_params + (OSCAR_BLOCK_K_NORM - OSCAR_BLOCK_K_SZ))[t] = n16_bits;
       sm.inv_n[t] = inv;
@@ -250,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
   for (int pass = 0; pass < 2; ++pass) {
     const int t = wave * 32 + pass * 16 + slot;
     double x[32];
-    key_fwht(ksrc + static_cast<int64_t>(t) * a.st, L, x);   // bit-identical to the first pass
+    key_fwht(ksrc + static_cast<int64_t>(t) * a.st, L, rotate, x);   // bit-identical to the first pass
     const double inv = sm.inv_n[t];
     uint32_t w0 = 0, w1 = 0;
 #pragma unroll

@@ -14,6 +14,7 @@ import dataclasses
 import numpy as np
 
 from .attention import decode_slice, dequant_keys_rotated, dequant_values
+from .hadamard import hadamard
 from .fp16 import fp16_bits, fp16_from_bits
 from .pack import pack_k_codes, pack_v_codes, unpack_k_codes, unpack_v_codes
 from .quantize import quantize_keys, quantize_values
@@ -33,6 +34,7 @@ class OracleSlice:
     v_tail: np.ndarray
     kq: dict = None       # key quantizer intermediates
     vq: dict = None       # value quantizer intermediates
+    rotated: bool = True  # keys stored in the rotated domain (the method; False only for the ablation)
 
     def dequantized(self):
         """(k^ rotated, v^) recovered from the packed bytes alone."""
@@ -49,17 +51,22 @@ class OracleSlice:
     def decode(self, q, sm_scale):
         """Attention of q [G, 128] (bf16-exact) over this slice."""
         k_hat, v_hat = self.dequantized()
+        if not self.rotated:
+            # keys stored as they are: H^T brings them to the rotated domain
+            # that decode_slice scores against (H is orthonormal)
+            k_hat = k_hat @ hadamard(k_hat.shape[-1]).T
         return decode_slice(q, k_hat, v_hat, self.k_tail, self.v_tail, sm_scale)
 
 
-def quantize_slice(k, v, n_quant, keep_intermediates=False):
+def quantize_slice(k, v, n_quant, keep_intermediates=False, rotate=True, scale=True):
     """Quantize the first n_quant tokens (a multiple of 128) of one slice;
-    the remaining tokens form the bf16 tail.  k, v: float64 [T, 128]."""
+    the remaining tokens form the bf16 tail.  k, v: float64 [T, 128].
+    rotate / scale: the key-quantizer variants of ``quantize_keys``."""
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     if n_quant % GROUP:
         raise ValueError("n_quant must be a multiple of 128")
-    kq = quantize_keys(k[:n_quant])
+    kq = quantize_keys(k[:n_quant], rotate=rotate, scale=scale)
     vq = quantize_values(v[:n_quant])
     G = n_quant // GROUP
     k_sz = np.stack([fp16_bits(kq["s16"]), fp16_bits(kq["z16"])], axis=-1).reshape(G, 128, 2)
@@ -74,4 +81,5 @@ def quantize_slice(k, v, n_quant, keep_intermediates=False):
         k_tail=k[n_quant:], v_tail=v[n_quant:],
         kq=kq if keep_intermediates else None,
         vq=vq if keep_intermediates else None,
+        rotated=rotate,
     )

@@ -94,15 +94,26 @@ def key_codes(u, s16, z16, group=GROUP):
     return _codes(u, np.asarray(s16)[g], np.asarray(z16)[g])
 
 
-def quantize_keys(k, group=GROUP):
+def quantize_keys(k, group=GROUP, rotate=True, scale=True):
     """Full key quantizer for k [T, 128] (T a multiple of 128, bf16-exact values).
 
     Returns a dict with every intermediate: y, n, n16, u, s_pre, z_pre, s16,
     z16, r, codes.
+
+    rotate / scale switch the two OScaR steps off for the Token Norm
+    Imbalance ablation (ai-papers.net OScaR summary, sections
+    "TNIという根本課題の特定" and "OScaRの提案手法"): without the rotation
+    y = k; without the scaling the stored norm is 1 (n = n16 = 1) and u = y,
+    so that dequantization n16 (s16 c + z16) is the same formula for every
+    variant.  Both on (the default) is the method.
     """
-    y = rotate_keys(k)
-    n, n16 = token_norms(y)
-    u = scale_tokens(y, n16)
+    y = rotate_keys(k) if rotate else np.asarray(k, dtype=np.float64)
+    if scale:
+        n, n16 = token_norms(y)
+        u = scale_tokens(y, n16)
+    else:
+        n = n16 = np.ones(y.shape[0])
+        u = y
     s_pre, z_pre, s16, z16 = key_group_params(u, group)
     r, codes = key_codes(u, s16, z16, group)
     return dict(y=y, n=n, n16=n16, u=u, s_pre=s_pre, z_pre=z_pre, s16=s16,

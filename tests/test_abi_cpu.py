@@ -68,7 +68,7 @@ needs_no_gpu = pytest.mark.skipif(not _no_gpu(), reason="placeholder pointers ar
 
 
 def _desc(**kw):
-    d = dict(batch=1, num_kv_heads=8, head_dim=128, group=128, capacity=1024,
+    d = dict(batch=1, num_kv_heads=8, head_dim=128, group=128, capacity=1024, flags=0,
              blocks=0x10000, k_tail=0x60000, v_tail=0x70000)
     d.update(kw)
     return ob.KVCacheDesc(*[d[f] for f, _ in ob.KVCacheDesc._fields_])
@@ -92,6 +92,8 @@ def test_decode_validation_errors():
     assert _decode(_desc(blocks=0x10080)) == ob.OSCAR_EINVAL        # blocks not 256-byte aligned
     assert b"256-byte" in L.oscar_last_error()
     assert _decode(_desc(k_tail=0x60008)) == ob.OSCAR_EINVAL        # tail not 16-byte aligned
+    assert _decode(_desc(flags=4)) == ob.OSCAR_EINVAL                # unknown key-variant bit
+    assert b"flags" in L.oscar_last_error()
     assert _decode(_desc(), hq=30) == ob.OSCAR_EUNSUPPORTED           # not a multiple of 8 KV heads
     assert _decode(_desc(), hq=24) == ob.OSCAR_EUNSUPPORTED           # 3 query heads per KV head
     assert _decode(_desc(), max_tokens=-1) == ob.OSCAR_EINVAL

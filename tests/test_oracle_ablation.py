@@ -57,3 +57,43 @@ def test_attention_weights_distance_is_a_distance():
     for var in A.VARIANTS:
         tv = A.attention_tv(q, k, var, 1 / np.sqrt(128))
         assert 0.0 <= tv <= 1.0
+
+
+FLAGS = {"per_channel": (False, False), "rotation": (True, False), "scaling": (False, True), "oscar": (True, True)}
+
+
+def test_quantizer_variants_closed_forms():
+    """quantize_keys(rotate, scale): u is k itself, k / fp16(||k||), H k, or
+    H k / fp16(||H k||); the stored norm is 1 whenever the scaling is off."""
+    k = _keys()[:256]
+    H = hadamard(128)
+    for var, (rot, sc) in FLAGS.items():
+        kq = oracle.quantize_keys(k, rotate=rot, scale=sc)
+        y = k @ H.T if rot else k
+        if sc:
+            n16 = oracle.fp16_rne(np.linalg.norm(y, axis=1))
+            np.testing.assert_allclose(kq["n16"], n16, rtol=0, atol=0)
+            np.testing.assert_allclose(kq["u"], y / n16[:, None], rtol=1e-15, atol=0)
+        else:
+            assert np.all(kq["n16"] == 1.0) and np.all(kq["n"] == 1.0)
+            np.testing.assert_array_equal(kq["u"], y)
+        # min / max per group and channel land on levels 0 and 3
+        codes = kq["codes"].reshape(2, 128, 128)
+        assert codes.min() == 0 and codes.max() == 3
+
+
+def test_variant_slices_decode_like_attention_over_their_dequantized_keys():
+    """OracleSlice.decode of every variant equals plain attention (no
+    Hadamard anywhere) of q over the variant's dequantized keys in k's basis
+    and the dequantized values."""
+    w = syn.workload(0)
+    k = _keys()
+    v = syn.bf16_bits_to_f64(syn.values_slice(w, 0, 0))
+    q = syn.bf16_bits_to_f64(syn.query(w, 0))
+    sm = 1 / np.sqrt(128)
+    vq = oracle.quantize_values(v)
+    v_hat = oracle.dequant_values(vq["codes"], vq["vs16"], vq["vz16"])
+    for var, (rot, sc) in FLAGS.items():
+        s = oracle.quantize_slice(k, v, k.shape[0], rotate=rot, scale=sc)
+        ref = oracle.decode_bf16_slice(q, A.quantize_dequantize_keys(k, var), v_hat, sm)
+        np.testing.assert_allclose(s.decode(q, sm), ref, rtol=0, atol=1e-12)

@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--ablation", action="store_true",
                    help="Token Norm Imbalance ablation on the 128K layer: attention-output error of each "
                         "key-quantizer variant against the bf16 kernel on the same keys and values")
+    p.add_argument("--append", action="store_true",
+                   help="32K + 57-token tail workload: 128 decode steps that append one token each "
+                        "(one group completes and is quantized); per-step time eager and replayed")
     p.add_argument("--sweep", action="store_true",
                    help="context sweep 8K..128K at batch 1 and 8: INT2 and bf16 decode steps, speed-up and "
                         "cache footprint (one JSON line per configuration instead of the benchmark line)")
@@ -220,6 +223,158 @@ def context_sweep(args):
             torch.cuda.empty_cache()
 
 
+def append_loop(args):
+    """The group-append workload (32768 quantized tokens + a 57-token bf16
+    tail, Llama-3.1-8B layer): each of 128 steps adds one new token to the
+    tail and decodes; the tail is quantized once, when it completes.  The
+    step writes its token inside the decode launch (oscar_decode_attn_append);
+    the same loop with separate tail copies and oscar_decode_attn is timed
+    for comparison.  Reports the mean step time eager and replayed from a
+    HIP graph, and the one-group quantize (8 KV heads) alone."""
+    import numpy as np
+    import torch
+    import synthetic as syn
+    from kv_cache_int2_fwht_amd import binding as ob
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = syn.workload(2)
+    B, H, Hq = w.batch, w.num_kv_heads, w.num_q_heads
+    L0 = w.lengths[0]
+    n_q0, tail0 = syn.split_lengths(L0)
+    steps = w.append_steps
+    cap = ((w.total_tokens(0) + 127) // 128) * 128
+    sm = 1.0 / np.sqrt(128.0)
+    k_dev = torch.stack([torch.from_numpy(syn.keys_slice(w, 0, h).view(np.int16)) for h in range(H)])[None]
+    v_dev = torch.stack([torch.from_numpy(syn.values_slice(w, 0, h).view(np.int16)) for h in range(H)])[None]
+    k_dev = k_dev.to(dev).view(torch.bfloat16)
+    v_dev = v_dev.to(dev).view(torch.bfloat16)
+    cache = ob.PackedCache(B, H, cap, device=dev)
+    ob.quantize_kv(cache, k_dev, v_dev, torch.zeros(1, dtype=torch.int32, device=dev),
+                   torch.full((1,), n_q0 // 128, dtype=torch.int32, device=dev), n_q0 // 128)
+    cache.k_tail[0, :, :tail0] = k_dev[0, :, n_q0:L0]
+    cache.v_tail[0, :, :tail0] = v_dev[0, :, n_q0:L0]
+    snapshot = [t.clone() for t in (cache.blocks, cache.k_tail, cache.v_tail)]
+    plan, n_quant, n_tail = [], n_q0, tail0
+    for s in range(steps):
+        slot = n_tail
+        n_tail += 1
+        append = n_tail == 128
+        if append:
+            n_quant, n_tail = n_quant + 128, 0
+        plan.append((slot, append, n_quant, n_tail))
+    nq_dev = torch.tensor([[p[2]] for p in plan], dtype=torch.int32, device=dev)
+    nt_dev = torch.tensor([[p[3]] for p in plan], dtype=torch.int32, device=dev)
+    q_dev = torch.stack([torch.from_numpy(syn.query(w, 0, s).view(np.int16)) for s in range(steps)])
+    q_dev = q_dev.to(dev).view(torch.bfloat16)[:, None].contiguous()
+    start = torch.full((1,), n_q0 // 128, dtype=torch.int32, device=dev)
+    one = torch.ones(1, dtype=torch.int32, device=dev)
+    outs = torch.zeros((steps, B, Hq, 128), dtype=torch.float32, device=dev)
+    ws = ob.alloc_workspace(B, H, Hq, cap, device=dev)
+
+    def loop_separate():
+        # tail copies, quantize when the tail is complete, then the decode
+        for s, (slot, append, nq, nt) in enumerate(plan):
+            cache.k_tail[0, :, slot] = k_dev[0, :, L0 + s]
+            cache.v_tail[0, :, slot] = v_dev[0, :, L0 + s]
+            if append:
+                ob.quantize_kv(cache, cache.k_tail, cache.v_tail, start, one, 1)
+            ob.decode_attn(cache, nq_dev[s], nt_dev[s], nq + nt, q_dev[s], sm, outs[s], ws)
+
+    # the append inside the decode launch: n_tail counts the new token (up to
+    # 128); a full tail is quantized after the step
+    plan_f, nq_f, nt_f = [], n_q0, tail0
+    for s in range(steps):
+        nt_f += 1
+        plan_f.append((nq_f, nt_f))
+        if nt_f == 128:
+            nq_f, nt_f = nq_f + 128, 0
+    nqf_dev = torch.tensor([[p[0]] for p in plan_f], dtype=torch.int32, device=dev)
+    ntf_dev = torch.tensor([[p[1]] for p in plan_f], dtype=torch.int32, device=dev)
+    new_k = k_dev[0, :, L0:L0 + steps].transpose(0, 1).contiguous()[:, None]   # [steps, 1, H, 128]
+    new_v = v_dev[0, :, L0:L0 + steps].transpose(0, 1).contiguous()[:, None]
+
+    def loop_fused():
+        for s, (nq, nt) in enumerate(plan_f):
+            ob.decode_attn_append(cache, nqf_dev[s], ntf_dev[s], nq + nt, q_dev[s], new_k[s], new_v[s], sm, outs[s],
+                                  ws)
+            if nt == 128:
+                ob.quantize_kv(cache, cache.k_tail, cache.v_tail, start, one, 1)
+
+    def restore():
+        for t, s0 in zip((cache.blocks, cache.k_tail, cache.v_tail), snapshot):
+            t.copy_(s0)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def time_loop(loop):
+        eager = []
+        for _ in range(3):
+            restore()
+            torch.cuda.synchronize()
+            e0.record()
+            loop()
+            e1.record()
+            torch.cuda.synchronize()
+            eager.append(e0.elapsed_time(e1) * 1e3 / steps)
+        g = torch.cuda.CUDAGraph()
+        restore()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            loop()
+        torch.cuda.current_stream().wait_stream(side)
+        restore()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            loop()
+        replay = []
+        for _ in range(3):
+            restore()
+            torch.cuda.synchronize()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            replay.append(e0.elapsed_time(e1) * 1e3 / steps)
+        return min(eager), min(replay)
+
+    eager_sep, replay_sep = time_loop(loop_separate)
+    eager, replay = time_loop(loop_fused)
+    # the decode step against the tail length (same cache, tail filled with
+    # the workload's next tokens)
+    restore()
+    cache.k_tail[0, :, :128] = k_dev[0, :, n_q0:n_q0 + 128]
+    cache.v_tail[0, :, :128] = v_dev[0, :, n_q0:n_q0 + 128]
+    by_tail = {}
+    for nt in (0, 1, 16, 57, 64, 127, 128):
+        nq_t = torch.full((1,), n_q0, dtype=torch.int32, device=dev)
+        nt_t = torch.full((1,), nt, dtype=torch.int32, device=dev)
+        for _ in range(10):
+            ob.decode_attn(cache, nq_t, nt_t, n_q0 + nt, q_dev[0], sm, outs[0], ws)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(100):
+            ob.decode_attn(cache, nq_t, nt_t, n_q0 + nt, q_dev[0], sm, outs[0], ws)
+        e1.record()
+        torch.cuda.synchronize()
+        by_tail[str(nt)] = round(e0.elapsed_time(e1) * 1e3 / 100, 2)
+    # the one-group quantize alone
+    qt = []
+    for _ in range(20):
+        e0.record()
+        ob.quantize_kv(cache, cache.k_tail, cache.v_tail, start, one, 1)
+        e1.record()
+        torch.cuda.synchronize()
+        qt.append(e0.elapsed_time(e1) * 1e3)
+    print(json.dumps({"append": "32k+57, 128 steps",
+                      "us_per_step_eager": round(eager, 2), "us_per_step_graph_replay": round(replay, 2),
+                      "separate_copies": {"us_per_step_eager": round(eager_sep, 2),
+                                          "us_per_step_graph_replay": round(replay_sep, 2)},
+                      "group_quantize_us_median": round(sorted(qt)[len(qt) // 2], 2),
+                      "decode_us_by_tail_tokens": by_tail}), flush=True)
+
+
 def ablation(args):
     """Attention-output error of the four key-quantizer variants (no rotation
     and no scaling = plain per-channel INT2; rotation only; scaling only;
@@ -310,6 +465,9 @@ def main():
         return
     if args.ablation:
         ablation(args)
+        return
+    if args.append:
+        append_loop(args)
         return
 
     import numpy as np

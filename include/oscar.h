@@ -104,8 +104,8 @@ typedef struct oscar_kv_cache {
   int32_t capacity;        /* tokens per sequence; a positive multiple of 128 */
   int32_t flags;           /* OSCAR_KEYS_* bits; the quantizer and the decode of a cache must agree */
   uint8_t* blocks;          /* [batch][num_kv_heads][capacity/128][OSCAR_BLOCK_BYTES] */
-  const uint16_t* k_tail;  /* read by oscar_decode_attn only; may be NULL if no tail is ever used */
-  const uint16_t* v_tail;
+  uint16_t* k_tail;        /* read by the decode calls, written by oscar_decode_attn_append only; */
+  uint16_t* v_tail;        /* may be NULL if no tail is ever used */
 } oscar_kv_cache;
 
 /* Version of this ABI (OSCAR_ABI_VERSION). */
@@ -177,7 +177,7 @@ size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_kv_heads,
  *
  * n_quant      : device int32[batch]; quantized tokens, a multiple of 128,
  *                <= capacity (precondition).
- * n_tail       : device int32[batch]; tail tokens, 0..127 (precondition).
+ * n_tail       : device int32[batch]; tail tokens, 0..128 (precondition).
  * max_tokens   : host upper bound of n_quant[b] + n_tail[b]; sizes the grid
  *                and the workspace.  Tokens beyond it are not read.
  * q            : bf16 [batch][num_q_heads][128].
@@ -193,6 +193,31 @@ oscar_status oscar_decode_attn(const oscar_kv_cache* cache,
                                int32_t max_tokens, const uint16_t* q,
                                int32_t num_q_heads, float sm_scale, float* out,
                                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * oscar_decode_attn_append -- a decode step that first appends the step's
+ * own key and value to the bf16 tail, in the same launch (the decode-time
+ * append of the group-append workflow: the pages quantize a group once it
+ * is complete, ai-papers.net OScaR summary, section "OScaRの提案手法").
+ *
+ * n_tail[b] counts the new token: it is stored at tail index n_tail[b] - 1
+ * of every KV head of sequence b and attended together with the rest.
+ * Preconditions: 1 <= n_tail[b] <= 128 and n_quant[b] + 128 <= capacity
+ * (the tail's group lies inside the cache).  When n_tail[b] reaches 128 the
+ * caller quantizes the tail (oscar_quantize_kv with k_tail / v_tail as the
+ * source and destination group n_quant[b] / 128) before the next append,
+ * and continues with n_quant[b] + 128 and n_tail[b] = 0.
+ *
+ * k_new, v_new : bf16 [batch][num_kv_heads][128], 16-byte aligned.
+ * cache->k_tail and cache->v_tail must be given.  Other arguments and the
+ * result as in oscar_decode_attn.
+ */
+oscar_status oscar_decode_attn_append(const oscar_kv_cache* cache,
+                                      const int32_t* n_quant, const int32_t* n_tail,
+                                      int32_t max_tokens, const uint16_t* q,
+                                      const uint16_t* k_new, const uint16_t* v_new,
+                                      int32_t num_q_heads, float sm_scale, float* out,
+                                      void* ws, size_t ws_bytes, void* stream);
 
 /*
  * The two halves of oscar_decode_attn, for callers that combine partial

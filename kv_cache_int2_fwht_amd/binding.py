@@ -52,7 +52,7 @@ class KVCacheDesc(ctypes.Structure):
 EXPORTED = (
     "oscar_abi_version", "oscar_status_string", "oscar_last_error",
     "oscar_quantize_kv", "oscar_decode_workspace_bytes",
-    "oscar_decode_attn", "oscar_decode_attn_bf16",
+    "oscar_decode_attn", "oscar_decode_attn_append", "oscar_decode_attn_bf16",
     "oscar_decode_num_splits", "oscar_decode_attn_splits", "oscar_decode_merge",
 )
 
@@ -83,6 +83,9 @@ def lib():
     L.oscar_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.oscar_decode_attn.restype = ctypes.c_int
     L.oscar_decode_attn.argtypes = [ctypes.POINTER(KVCacheDesc), vp, vp, i32, vp, i32, f32, vp, vp, sz, vp]
+    L.oscar_decode_attn_append.restype = ctypes.c_int
+    L.oscar_decode_attn_append.argtypes = [ctypes.POINTER(KVCacheDesc), vp, vp, i32, vp, vp, vp, i32, f32, vp, vp,
+                                           sz, vp]
     L.oscar_decode_attn_bf16.restype = ctypes.c_int
     L.oscar_decode_attn_bf16.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp, sz, vp]
     L.oscar_decode_num_splits.restype = i32
@@ -242,6 +245,27 @@ def decode_attn(cache: PackedCache, n_quant: torch.Tensor, n_tail: torch.Tensor,
                                    _ptr(q, torch.bfloat16, "q"), q.shape[1], float(sm_scale),
                                    _ptr(out, torch.float32, "out"), _ptr(ws, torch.uint8, "ws"),
                                    ws.numel(), _stream(stream)))
+
+
+def decode_attn_append(cache: PackedCache, n_quant: torch.Tensor, n_tail: torch.Tensor, max_tokens: int,
+                       q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, sm_scale: float,
+                       out: torch.Tensor, ws: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """oscar_decode_attn_append.  k_new / v_new bf16 [B, Hkv, 128] (the step's
+    own key and value, stored at tail index n_tail - 1 and attended)."""
+    if q.dim() != 3 or q.shape[0] != cache.batch or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [batch, q_heads, 128]")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (cache.batch, cache.num_kv_heads, HEAD_DIM):
+            raise ValueError(f"{name} must be [batch, kv_heads, 128]")
+    d = cache.desc()
+    _check(lib().oscar_decode_attn_append(ctypes.byref(d), _ptr(n_quant, torch.int32, "n_quant"),
+                                          _ptr(n_tail, torch.int32, "n_tail"), int(max_tokens),
+                                          _ptr(q, torch.bfloat16, "q"), _ptr(k_new, torch.bfloat16, "k_new"),
+                                          _ptr(v_new, torch.bfloat16, "v_new"), q.shape[1], float(sm_scale),
+                                          _ptr(out, torch.float32, "out"), _ptr(ws, torch.uint8, "ws"),
+                                          ws.numel(), _stream(stream)))
 
 
 def decode_attn_bf16(k: torch.Tensor, v: torch.Tensor, seq_len: torch.Tensor, max_tokens: int,

@@ -49,32 +49,41 @@ oscar_status launched(hipError_t e, const char* fn) {
   return ok();
 }
 
-// About one 8-wave workgroup per compute unit: each wave then streams
-// several groups back to back (prefetching the next while computing the
-// current), and no younger workgroup waits behind an older one on a CU.
+// One workgroup per compute unit (256 on MI355X), all resident at once: as
+// many splits per (sequence, KV head) as fit, so that no workgroup waits for
+// another to finish.  A split covers whole 128-token groups.
 #ifndef OSCAR_TARGET_BLOCKS
 #define OSCAR_TARGET_BLOCKS 256
 #endif
 constexpr int64_t kTargetBlocks = OSCAR_TARGET_BLOCKS;
-constexpr int64_t kMinBlocks = OSCAR_TARGET_BLOCKS;
 
 SplitPlan make_plan(int32_t batch, int32_t num_kv_heads, int32_t max_tokens) {
   const int64_t heads = static_cast<int64_t>(batch) * num_kv_heads;
   const int64_t T = max_tokens > 0 ? max_tokens : 0;
-  auto nsplit = [&](int64_t tps) { return (T + tps - 1) / tps; };
-  int64_t tps = 512;
-  while (heads * nsplit(tps) > kTargetBlocks && tps < (int64_t{1} << 24)) tps *= 2;
-  while (tps > OSCAR_GROUP && heads * nsplit(tps) < kMinBlocks && nsplit(tps / 2) > nsplit(tps)) tps /= 2;
+  const int64_t groups = (T + OSCAR_GROUP - 1) / OSCAR_GROUP;
+  int64_t s = kTargetBlocks / (heads > 0 ? heads : 1);
+  s = s < 1 ? 1 : s;
+  s = (groups > 0 && s > groups) ? groups : s;
+  const int64_t tps = ((groups + s - 1) / s) * OSCAR_GROUP;   // whole groups per split
   SplitPlan p;
-  p.tokens_per_split = static_cast<int32_t>(tps);
-  p.splits = static_cast<int32_t>(nsplit(tps) > 0 ? nsplit(tps) : 1);
+  p.tokens_per_split = static_cast<int32_t>(tps > 0 ? tps : OSCAR_GROUP);
+  p.splits = static_cast<int32_t>(T > 0 ? (T + p.tokens_per_split - 1) / p.tokens_per_split : 1);
   return p;
 }
 
 }  // namespace
 
 SplitPlan plan_int2(int32_t batch, int32_t num_kv_heads, int32_t max_tokens) {
-  return make_plan(batch, num_kv_heads, max_tokens);
+  // The INT2 kernel deals the groups out round-robin (split s takes groups
+  // s, s + S, ...), so it uses every split that fits, up to one per group.
+  SplitPlan p = make_plan(batch, num_kv_heads, max_tokens);
+  const int64_t heads = static_cast<int64_t>(batch) * num_kv_heads;
+  const int64_t groups = (static_cast<int64_t>(max_tokens > 0 ? max_tokens : 0) + OSCAR_GROUP - 1) / OSCAR_GROUP;
+  int64_t s = kTargetBlocks / (heads > 0 ? heads : 1);
+  s = s < 1 ? 1 : s;
+  s = (groups > 0 && s > groups) ? groups : s;
+  p.splits = static_cast<int32_t>(groups > 0 ? s : 1);
+  return p;
 }
 SplitPlan plan_bf16(int32_t batch, int32_t num_kv_heads, int32_t max_tokens) {
   return make_plan(batch, num_kv_heads, max_tokens);
@@ -192,7 +201,7 @@ namespace {
 // is checked only when the caller also merges.
 oscar_status decode_int2_splits(const char* fn, const oscar_kv_cache* cache, const int32_t* n_quant,
                                 const int32_t* n_tail, int32_t max_tokens, const uint16_t* q, int32_t num_q_heads,
-                                float sm_scale, const float* out, bool with_out, void* ws, size_t ws_bytes,
+                                float sm_scale, const uint16_t* k_new, const uint16_t* v_new, const float* out, bool with_out, void* ws, size_t ws_bytes,
                                 hipStream_t s, int32_t* splits_out) {
   oscar_status st = check_cache(fn, cache);
   if (st != OSCAR_OK) return st;
@@ -211,6 +220,8 @@ oscar_status decode_int2_splits(const char* fn, const oscar_kv_cache* cache, con
   a.blocks = cache->blocks;
   a.k_tail = cache->k_tail;
   a.v_tail = cache->v_tail;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.n_quant = n_quant;
   a.n_tail = n_tail;
   a.q = q;
@@ -241,7 +252,8 @@ oscar_status oscar_decode_attn_splits(const oscar_kv_cache* cache, const int32_t
                                       void* ws, size_t ws_bytes, void* stream) {
   int32_t splits = 0;
   return decode_int2_splits("oscar_decode_attn_splits", cache, n_quant, n_tail, max_tokens, q, num_q_heads,
-                            sm_scale, nullptr, false, ws, ws_bytes, static_cast<hipStream_t>(stream), &splits);
+                            sm_scale, nullptr, nullptr, nullptr, false, ws, ws_bytes, static_cast<hipStream_t>(stream),
+                            &splits);
 }
 
 oscar_status oscar_decode_merge(const float* partials, int32_t batch, int32_t num_q_heads, int32_t num_splits,
@@ -264,8 +276,25 @@ oscar_status oscar_decode_attn(const oscar_kv_cache* cache, const int32_t* n_qua
   const char* fn = "oscar_decode_attn";
   const hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t splits = 0;
-  oscar_status st = decode_int2_splits(fn, cache, n_quant, n_tail, max_tokens, q, num_q_heads, sm_scale, out, true,
-                                       ws, ws_bytes, s, &splits);
+  oscar_status st = decode_int2_splits(fn, cache, n_quant, n_tail, max_tokens, q, num_q_heads, sm_scale, nullptr,
+                                       nullptr, out, true, ws, ws_bytes, s, &splits);
+  if (st != OSCAR_OK) return st;
+  return launched(launch_merge(static_cast<const float*>(ws), out, cache->batch, num_q_heads, splits, s), fn);
+}
+
+oscar_status oscar_decode_attn_append(const oscar_kv_cache* cache, const int32_t* n_quant, const int32_t* n_tail,
+                                      int32_t max_tokens, const uint16_t* q, const uint16_t* k_new,
+                                      const uint16_t* v_new, int32_t num_q_heads, float sm_scale, float* out,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "oscar_decode_attn_append";
+  if (!k_new || !v_new) return fail(OSCAR_EINVAL, "%s: NULL k_new or v_new", fn);
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(OSCAR_EINVAL, "%s: k_new and v_new must be 16-byte aligned", fn);
+  if (cache && (!cache->k_tail || !cache->v_tail))
+    return fail(OSCAR_EINVAL, "%s: the cache has no tail buffers to append to", fn);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t splits = 0;
+  oscar_status st = decode_int2_splits(fn, cache, n_quant, n_tail, max_tokens, q, num_q_heads, sm_scale, k_new,
+                                       v_new, out, true, ws, ws_bytes, s, &splits);
   if (st != OSCAR_OK) return st;
   return launched(launch_merge(static_cast<const float*>(ws), out, cache->batch, num_q_heads, splits, s), fn);
 }

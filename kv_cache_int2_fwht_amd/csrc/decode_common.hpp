@@ -164,62 +164,103 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
-// bf16 tokens (the not yet quantized tail) with plain VALU arithmetic: one
-// wave scores up to 128 tokens with the unrotated query (lane = token) and
-// accumulates their values (lane = channel pair), leaving a softmax state in
-// `slot` of the merge buffer.  k, v: token-major bf16 rows of 128 channels.
+// bf16 tokens (the not yet quantized tail): one wave scores up to 64
+// tokens on the matrix cores, exact bf16 x bf16 products of the query (not
+// rotated, since the tail is stored as it is) and the keys accumulated in
+// fp32, then accumulates the values with plain VALU arithmetic (lane =
+// channel pair), leaving a softmax state in `slot` of the merge buffer.
+// k, v: token-major bf16 rows of 128 channels; q: the G query rows (bf16);
+// scale: sm_scale * log2(e).  Token `last` is read from the rows k_last /
+// v_last instead when they are given (a token appended in the same launch).
+// pv: LDS scratch of the weights, [64 tokens][G].
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kTailPart = 64;   // tokens per bf16_tokens_wave call
+
 template <int G, int kSlots>
-__device__ void bf16_tokens_wave(const uint16_t* k, const uint16_t* v, int n_tok, const float (*q_raw)[kHeadDim],
-                                 float (*pv)[kGroup], MergeSmem<G, kSlots>& sm, int slot) {
+__device__ void bf16_tokens_wave(const uint16_t* k, const uint16_t* v, int n_tok, const uint16_t* q, float scale,
+                                 float (*pv)[G], MergeSmem<G, kSlots>& sm, int slot,
+                                 const uint16_t* k_last = nullptr, const uint16_t* v_last = nullptr, int last = -1) {
+  static_assert(G <= 8, "query rows 0..G-1 of the 16-row operand, two row groups at most");
+  constexpr int kTiles = kTailPart / 16;
+  n_tok = min(n_tok, kTailPart);
   const int lane = threadIdx.x & 63;
-  float logit[G][2];
+  const int gl = lane >> 4;   // operand K slice / result row group (heads 4 gl .. 4 gl + 3)
+  const int n = lane & 15;    // operand row (query head) / result column (token of the tile)
+  // every load first: the query (A operand: head n, zero rows beyond G,
+  // channels 32 ks + 8 gl .. +7), the key rows of the tiles (B operand) and
+  // the value pairs of all tokens (lane = channel pair); tokens past n_tok
+  // read row 0 and are masked
+  uint4 qa[4], kb[kTiles][4];
+  uint32_t vv[kTailPart];
+  {
+    const uint16_t* qrow = q + static_cast<size_t>(n < G ? n : 0) * kHeadDim + 8 * gl;
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int tt = lane + 64 * kk;
-    const bool valid = tt < n_tok;
-    float dot[G];
+    for (int ks = 0; ks < 4; ++ks) qa[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks);
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) dot[hh] = 0.f;
-    if (valid) {
-      const uint4* kr = reinterpret_cast<const uint4*>(k + static_cast<size_t>(tt) * kHeadDim);
-#pragma unroll 4
-      for (int c = 0; c < 16; ++c) {
-        const uint4 w = kr[c];
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    for (int j = 0; j < kTiles; ++j) {
+      const int tok = 16 * j + n;
+      const uint16_t* krow = (k_last != nullptr && tok == last) ? k_last
+                                                                : k + static_cast<size_t>(tok < n_tok ? tok : 0) * kHeadDim;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float k0 = bf16lo_to_f32(ws[e]), k1 = bf16hi_to_f32(ws[e]);
-#pragma unroll
-          for (int hh = 0; hh < G; ++hh) {
-            dot[hh] = fmaf(q_raw[hh][8 * c + 2 * e], k0, dot[hh]);
-            dot[hh] = fmaf(q_raw[hh][8 * c + 2 * e + 1], k1, dot[hh]);
-          }
-        }
-      }
+      for (int ks = 0; ks < 4; ++ks) kb[j][ks] = *reinterpret_cast<const uint4*>(krow + 32 * ks + 8 * gl);
     }
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) logit[hh][kk] = valid ? dot[hh] : -INFINITY;
+    for (int e = 0; e < kTailPart; ++e) {
+      const uint16_t* vrow = (v_last != nullptr && e == last) ? v_last
+                                                               : v + static_cast<size_t>(e < n_tok ? e : 0) * kHeadDim;
+      vv[e] = *reinterpret_cast<const uint32_t*>(vrow + 2 * lane);
+    }
   }
-  float mx[G], lsum[G];
+  // scores: tile j = tokens 16 j .. 16 j + 15; lane holds rows 4 gl + r of column n
+  float lg[kTiles][4];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    mx[hh] = wave_max(fmaxf(logit[hh][0], logit[hh][1]));
-    const float p0 = (mx[hh] == -INFINITY) ? 0.f : exp2f(logit[hh][0] - mx[hh]);
-    const float p1 = (mx[hh] == -INFINITY) ? 0.f : exp2f(logit[hh][1] - mx[hh]);
-    lsum[hh] = wave_sum(p0 + p1);
-    pv[hh][lane] = p0;
-    pv[hh][lane + 64] = p1;
+  for (int j = 0; j < kTiles; ++j) {
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, n < G ? qa[ks] : make_uint4(0, 0, 0, 0)),
+                                                  __builtin_bit_cast(bf16x8_t, kb[j][ks]), c, 0, 0, 0);
+    const bool valid = 16 * j + n < n_tok;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lg[j][r] = valid ? c[r] * scale : -INFINITY;
+  }
+  // softmax per head (max and sum over the tiles in-lane, then over the 16 lanes of the row)
+  float mx[4], ls[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float m = lg[0][r];
+#pragma unroll
+    for (int j = 1; j < kTiles; ++j) m = fmaxf(m, lg[j][r]);
+    mx[r] = row_max16(m);   // finite: token 0 of the part is always valid
+    float l = 0.f;
+#pragma unroll
+    for (int j = 0; j < kTiles; ++j) {
+      const float p = fast_exp2(lg[j][r] - mx[r]);   // 0 for masked tokens
+      lg[j][r] = p;
+      l += p;
+    }
+    ls[r] = row_sum16(l);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int hh = 4 * gl + r;
+    if (hh < G) {
+#pragma unroll
+      for (int j = 0; j < kTiles; ++j) pv[16 * j + n][hh] = lg[j][r];   // masked tokens get 0
+    }
   }
   wave_sync_lds();
+  // values
   float add[G][2];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) add[hh][0] = add[hh][1] = 0.f;
-  for (int tt = 0; tt < n_tok; ++tt) {
-    const uint32_t vv = *reinterpret_cast<const uint32_t*>(v + static_cast<size_t>(tt) * kHeadDim + 2 * lane);
-    const float v0 = bf16lo_to_f32(vv), v1 = bf16hi_to_f32(vv);
+#pragma unroll
+  for (int e = 0; e < kTailPart; ++e) {
+    const float v0 = bf16lo_to_f32(vv[e]), v1 = bf16hi_to_f32(vv[e]);
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float p = pv[hh][tt];
+      const float p = pv[e][hh];   // 0 past n_tok
       add[hh][0] = fmaf(p, v0, add[hh][0]);
       add[hh][1] = fmaf(p, v1, add[hh][1]);
     }
@@ -228,9 +269,13 @@ __device__ void bf16_tokens_wave(const uint16_t* k, const uint16_t* v, int n_tok
   for (int hh = 0; hh < G; ++hh) {
     sm.acc[slot][hh][2 * lane] = add[hh][0];
     sm.acc[slot][hh][2 * lane + 1] = add[hh][1];
-    if (lane == 0) {
-      sm.m[slot][hh] = mx[hh];
-      sm.l[slot][hh] = lsum[hh];
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int hh = 4 * gl + r;
+    if (hh < G && n == 0) {
+      sm.m[slot][hh] = mx[r];
+      sm.l[slot][hh] = ls[r];
     }
   }
 }

@@ -313,7 +313,7 @@ struct Int2Cfg {
   static constexpr int kLoaders = 2;
   static constexpr int kCompute = kWaves - kLoaders;
   static constexpr int kThreads = kWaves * kWave;
-  static constexpr int kSlots = kCompute + 1;  // one merge slot per compute wave + one for the bf16 tail
+  static constexpr int kSlots = kCompute + 2;  // one merge slot per compute wave + two for the bf16 tail
   static constexpr int kRing = (kRB == 1) ? 10 : 8;   // group stages in LDS (a multiple of kLoaders)
   static_assert(kWaves % 4 == 0 && kLoaders < 4, "compute waves on every SIMD");
   static constexpr int kAhead = 2;           // groups each loader has in flight (kAhead * kDmaPerGroup <= 63)
@@ -325,7 +325,7 @@ template <int G>
 struct Int2Smem {
   float q_raw[Int2Cfg<G>::kRows][kHeadDim];   // q * sm_scale * log2(e)
   float q_rot[Int2Cfg<G>::kRows][kHeadDim];   // (H q) * sm_scale * log2(e)
-  float tail_p[G][kGroup];                     // softmax weights of the bf16 tail tokens
+  float tail_p[kGroup][G];                     // softmax weights of the bf16 tail tokens (two halves)
   // per compute wave and row block: an MFMA A operand staged as
   // [half][lane group][row][16 bytes] (the scores' q digits, then the
   // values' p digits)
@@ -550,7 +550,7 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
                : "s"(a.n_quant + b), "s"(a.n_tail + b)
                : "memory");
   nq = min(max(nq, 0) & ~(kGroup - 1), a.capacity);
-  nt = min(max(nt, 0), kGroup - 1);
+  nt = min(max(nt, 0), kGroup);
   if (a.k_tail == nullptr || a.v_tail == nullptr) nt = 0;
   const int total = min(nq + nt, a.max_tokens);
   const int n_groups = (total + kGroup - 1) / kGroup;
@@ -593,20 +593,44 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
       __hip_atomic_store(&sm.filled[k % C::kRing], k / C::kRing + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // first groups requested for nothing included
-    if (wave == 0) {
-      // ---- the bf16 tail (at most one partial group, after the quantized
-      // ones) -> the last merge slot, while the compute waves still work ----
-      clear_slot(sm.merge, C::kCompute);   // stays empty unless a tail is seen
+  } else {
+    if (wave >= C::kWaves - 2) {
+      // ---- the bf16 tail (at most one group, after the quantized ones):
+      // tokens 0..63 -> merge slot kCompute (last wave), 64..127 -> slot
+      // kCompute + 1 (the wave before).  Done first, while the first groups
+      // are still on their way, by the two compute waves with the fewest
+      // groups ----
+      const int half = C::kWaves - 1 - wave;   // 0: tokens 0..63, 1: tokens 64..127
+      const int slot = C::kCompute + half;
+      clear_slot(sm.merge, slot);              // stays empty unless tail tokens are seen
       const int g_tail = nq / kGroup;
-      if (nt > 0 && g_tail < n_groups && g_tail % S == split) {
-        while (__hip_atomic_load(&sm.q_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
-          __builtin_amdgcn_s_sleep(1);
-        const int n_tok = min(nt, total - g_tail * kGroup);
-        bf16_tokens_wave<G, C::kSlots>(a.k_tail + slice * kGroup * kHeadDim, a.v_tail + slice * kGroup * kHeadDim,
-                                       n_tok, sm.q_raw, sm.tail_p, sm.merge, C::kCompute);
+      const bool owner = (g_tail % S == split);   // one workgroup per slice holds the tail
+      const size_t tail_row0 = slice * kGroup * kHeadDim;
+      const uint16_t* k_new = nullptr;
+      const uint16_t* v_new = nullptr;
+      if (a.k_new != nullptr && nt > 0 && owner) {
+        // the token appended in this launch: stored at tail index nt - 1 (by
+        // the first of the two waves), and attended from its source rows
+        k_new = a.k_new + slice * kHeadDim;
+        v_new = a.v_new + slice * kHeadDim;
+        if (half == 0) {
+          const size_t dst = tail_row0 + static_cast<size_t>(nt - 1) * kHeadDim + 2 * lane;
+          *reinterpret_cast<uint32_t*>(a.k_tail + dst) = *reinterpret_cast<const uint32_t*>(k_new + 2 * lane);
+          *reinterpret_cast<uint32_t*>(a.v_tail + dst) = *reinterpret_cast<const uint32_t*>(v_new + 2 * lane);
+        }
+      }
+      const int t_begin = kTailPart * half;
+      if (nt > 0 && g_tail < n_groups && owner) {
+        const int n_tok = min(nt, total - g_tail * kGroup) - t_begin;   // this wave's tokens
+        if (n_tok > 0) {
+          const size_t row0 = tail_row0 + static_cast<size_t>(t_begin) * kHeadDim;
+          bf16_tokens_wave<G, C::kSlots>(a.k_tail + row0, a.v_tail + row0, min(n_tok, kTailPart),
+                                         a.q + (static_cast<size_t>(b) * a.num_q_heads + qh0) * kHeadDim,
+                                         a.sm_scale * kLog2e, sm.tail_p + t_begin, sm.merge, slot, k_new, v_new,
+                                         nt - 1 - t_begin);
+        }
       }
     }
-  } else {
     if (cw == 0) {
       rotate_q_wave<RB>(q_in, a.sm_scale * kLog2e, sm.q_raw, sm.q_rot, lane);
       // every lane releases its own writes

@@ -41,8 +41,10 @@ struct QuantizeArgs {
 
 struct DecodeInt2Args {
   const uint8_t* blocks;
-  const uint16_t* k_tail;
-  const uint16_t* v_tail;
+  uint16_t* k_tail;        // written only when a token is appended (k_new given)
+  uint16_t* v_tail;
+  const uint16_t* k_new;   // token appended to the tail in this launch ([B][Hkv][128]), or null
+  const uint16_t* v_new;
   const int32_t* n_quant;
   const int32_t* n_tail;
   const uint16_t* q;

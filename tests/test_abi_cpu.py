@@ -81,6 +81,20 @@ def _decode(desc, hq=32, max_tokens=1024, ws_bytes=1 << 26, q=0x80000, out=0x900
 
 
 @needs_no_gpu
+def test_decode_append_validation_errors():
+    L = ob.lib()
+
+    def app(desc, k_new=0xB0000, v_new=0xC0000):
+        return L.oscar_decode_attn_append(ctypes.byref(desc), 0x100, 0x200, 1024, 0x80000, k_new, v_new, 32, 0.088,
+                                          0x90000, 0xA0000, 1 << 26, None)
+    assert app(_desc(), k_new=0) == ob.OSCAR_EINVAL
+    assert app(_desc(), v_new=0xC0008) == ob.OSCAR_EINVAL        # not 16-byte aligned
+    assert app(_desc(k_tail=0)) == ob.OSCAR_EINVAL                # nothing to append to
+    assert b"tail" in L.oscar_last_error()
+    assert app(_desc()) == ob.OSCAR_EHIP                          # valid, but no device here
+
+
+@needs_no_gpu
 def test_decode_validation_errors():
     L = ob.lib()
     assert _decode(None) == ob.OSCAR_EINVAL

@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--append", action="store_true",
                    help="32K + 57-token tail workload: 128 decode steps that append one token each "
                         "(one group completes and is quantized); per-step time eager and replayed")
+    p.add_argument("--batch8", action="store_true",
+                   help="batch 8 with jittered 96K-128K lengths (quantized groups plus bf16 tails): "
+                        "decode tokens/s per layer and HBM GB/s, against the bf16 kernel")
     p.add_argument("--sweep", action="store_true",
                    help="context sweep 8K..128K at batch 1 and 8: INT2 and bf16 decode steps, speed-up and "
                         "cache footprint (one JSON line per configuration instead of the benchmark line)")
@@ -221,6 +224,71 @@ def context_sweep(args):
                               "copies": [n_int2, n_bf16]}), flush=True)
             del caches, kv, ws
             torch.cuda.empty_cache()
+
+
+def batch8(args):
+    """Batch 8, lengths jittered in [96K, 128K] (the workload's seeded
+    lengths; n_quant = 128 floor(L / 128), the rest a bf16 tail), 32 query /
+    8 KV heads.  Every sequence holds the 128K generator's keys and values
+    (the step time does not depend on the values).  Algorithmic bytes per
+    step: sum over sequences of n_quant 8 74 B + n_tail 8 512 B, plus q and
+    out.  One JSON line."""
+    import numpy as np
+    import torch
+    import synthetic as syn
+    from kv_cache_int2_fwht_amd import binding as ob
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w4, w3 = syn.workload(4), syn.workload(3)
+    B, H, Hq = w4.batch, w4.num_kv_heads, w4.num_q_heads
+    lens = list(w4.lengths)
+    nqs = [syn.split_lengths(n)[0] for n in lens]
+    nts = [n - m for n, m in zip(lens, nqs)]
+    cap = ((max(lens) + 127) // 128) * 128
+    sm = 1.0 / np.sqrt(128.0)
+    src_k = torch.empty((H, cap, 128), dtype=torch.bfloat16, device=dev)
+    src_v = torch.empty_like(src_k)
+    for h in range(H):
+        src_k[h] = torch.from_numpy(syn.keys_slice(w3, 0, h)[:cap].view(np.int16)).to(dev).view(torch.bfloat16)
+        src_v[h] = torch.from_numpy(syn.values_slice(w3, 0, h)[:cap].view(np.int16)).to(dev).view(torch.bfloat16)
+    k = src_k.unsqueeze(0).expand(B, H, cap, 128).contiguous()
+    v = src_v.unsqueeze(0).expand(B, H, cap, 128).contiguous()
+    cache = ob.PackedCache(B, H, cap, device=dev)
+    i32 = lambda x: torch.tensor(x, dtype=torch.int32, device=dev)   # noqa: E731
+    ob.quantize_kv(cache, k, v, i32([0] * B), i32([n // 128 for n in nqs]), max(nqs) // 128)
+    for b in range(B):
+        cache.k_tail[b, :, :nts[b]] = k[b, :, nqs[b]:lens[b]]
+        cache.v_tail[b, :, :nts[b]] = v[b, :, nqs[b]:lens[b]]
+    q = torch.from_numpy(np.stack([syn.query(w4, b) for b in range(B)]).view(np.int16)).to(dev).view(torch.bfloat16)
+    q = q.contiguous()
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    ws = ob.alloc_workspace(B, H, Hq, max(lens), device=dev)
+    nq_t, nt_t, len_t = i32(nqs), i32(nts), i32(lens)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    int2_us = timed(lambda: ob.decode_attn(cache, nq_t, nt_t, max(lens), q, sm, out, ws), max(20, args.steps // 2))
+    bf16_us = timed(lambda: ob.decode_attn_bf16(k, v, len_t, max(lens), q, sm, out, ws), 20)
+    int2_bytes = sum(nq * H * BYTES_PER_TOKEN_HEAD + nt * H * BF16_BYTES_PER_TOKEN_HEAD
+                     for nq, nt in zip(nqs, nts)) + B * Hq * 128 * (2 + 4)
+    bf16_bytes = sum(lens) * H * BF16_BYTES_PER_TOKEN_HEAD + B * Hq * 128 * (2 + 4)
+    print(json.dumps({"batch8": "jittered 96K-128K", "lengths": lens, "tails": nts,
+                      "int2_us_per_step": round(int2_us, 2), "tokens_per_s": round(B / (int2_us * 1e-6), 1),
+                      "int2_GBs": round(int2_bytes / (int2_us * 1e-6) / 1e9, 1),
+                      "bf16_us_per_step": round(bf16_us, 2),
+                      "bf16_GBs": round(bf16_bytes / (bf16_us * 1e-6) / 1e9, 1),
+                      "speedup_vs_bf16": round(bf16_us / int2_us, 3)}), flush=True)
 
 
 def append_loop(args):
@@ -468,6 +536,9 @@ def main():
         return
     if args.append:
         append_loop(args)
+        return
+    if args.batch8:
+        batch8(args)
         return
 
     import numpy as np

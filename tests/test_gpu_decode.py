@@ -70,6 +70,10 @@ CASES = {
     "g1_tail": lambda: syn.custom_workload(2, 3, 3, [300, 2048 + 127], cfg_tag=103),
     "g2": lambda: syn.custom_workload(1, 4, 2, [5000], cfg_tag=104),
     "g8": lambda: syn.custom_workload(2, 16, 2, [1, 4096 + 64], cfg_tag=105),
+    # tails longer than 64 tokens are scored by two waves (both row groups at G = 8)
+    "g8_tail100": lambda: syn.custom_workload(1, 8, 1, [640 + 100], cfg_tag=106),
+    # a sequence made of a tail only (no quantized group), and a long tail after groups
+    "g2_tail90": lambda: syn.custom_workload(2, 4, 2, [90, 1280 + 90], cfg_tag=107),
 }
 
 

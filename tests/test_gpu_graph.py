@@ -93,3 +93,81 @@ def test_32k_append_loop_graph_replay_matches_eager(gpu_lib):
         assert torch.equal(outs, eager), f"replay {rep} differs from the eager run"
         _ = (k_dev.float().sum() + 1).item()   # eager work between replays
     _say("  3 replays equal the eager run")
+
+
+def test_32k_append_in_decode_loop_graph_replay_matches_eager(gpu_lib):
+    """The same workload with the token written inside the decode launch
+    (oscar_decode_attn_append): the tail reaches 128 tokens at step 70 and
+    is quantized after that step.  Replays equal the eager run bit for bit,
+    and the cache ends in the same state."""
+    from kv_cache_int2_fwht_amd import binding as ob
+    dev = torch.device("cuda:0")
+    w = syn.workload(2)
+    B, H, Hq = w.batch, w.num_kv_heads, w.num_q_heads
+    L0 = w.lengths[0]
+    n_q0, tail0 = syn.split_lengths(L0)
+    steps = w.append_steps
+    cap = ((w.total_tokens(0) + 127) // 128) * 128
+    _say(f"graph capture of {steps} append-in-decode steps at {L0} tokens")
+    k_dev = bits_to_dev_bf16(np.stack([syn.keys_slice(w, 0, h) for h in range(H)])[None], dev)
+    v_dev = bits_to_dev_bf16(np.stack([syn.values_slice(w, 0, h) for h in range(H)])[None], dev)
+    cache = ob.PackedCache(B, H, cap, device=dev)
+    ob.quantize_kv(cache, k_dev, v_dev, torch.zeros(1, dtype=torch.int32, device=dev),
+                   torch.full((1,), n_q0 // 128, dtype=torch.int32, device=dev), n_q0 // 128)
+    cache.k_tail[0, :, :tail0] = k_dev[0, :, n_q0:L0]
+    cache.v_tail[0, :, :tail0] = v_dev[0, :, n_q0:L0]
+    torch.cuda.synchronize()
+    snapshot = {n: getattr(cache, n).clone() for n in STATE}
+
+    plan, n_quant, n_tail = [], n_q0, tail0
+    for s in range(steps):
+        n_tail += 1
+        plan.append((n_quant, n_tail))
+        if n_tail == 128:
+            n_quant, n_tail = n_quant + 128, 0
+    nq_dev = torch.tensor([[p[0]] for p in plan], dtype=torch.int32, device=dev)
+    nt_dev = torch.tensor([[p[1]] for p in plan], dtype=torch.int32, device=dev)
+    q_dev = bits_to_dev_bf16(np.stack([syn.query(w, 0, s)[None] for s in range(steps)]), dev)
+    new_k = k_dev[0, :, L0:L0 + steps].transpose(0, 1).contiguous()[:, None]   # [steps, 1, H, 128]
+    new_v = v_dev[0, :, L0:L0 + steps].transpose(0, 1).contiguous()[:, None]
+    start = torch.full((1,), n_q0 // 128, dtype=torch.int32, device=dev)
+    one = torch.ones(1, dtype=torch.int32, device=dev)
+    outs = torch.zeros((steps, B, Hq, 128), dtype=torch.float32, device=dev)
+    ws = ob.alloc_workspace(B, H, Hq, cap, device=dev)
+
+    def loop():
+        for s, (nq, nt) in enumerate(plan):
+            ob.decode_attn_append(cache, nq_dev[s], nt_dev[s], nq + nt, q_dev[s], new_k[s], new_v[s], SM, outs[s], ws)
+            if nt == 128:
+                ob.quantize_kv(cache, cache.k_tail, cache.v_tail, start, one, 1)
+
+    def restore():
+        for n in STATE:
+            getattr(cache, n).copy_(snapshot[n])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        loop()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = outs.clone()
+    final = {n: getattr(cache, n).clone() for n in STATE}
+    assert torch.isfinite(eager).all()
+    restore()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        loop()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        restore()
+        outs.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs, eager), f"replay {rep} differs from the eager run"
+        for n in STATE:
+            assert torch.equal(getattr(cache, n), final[n]), f"replay {rep}: cache {n} differs"
+        _ = (k_dev.float().sum() + 1).item()   # eager work between replays
+    _say("  3 replays equal the eager run")

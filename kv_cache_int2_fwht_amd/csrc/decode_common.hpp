@@ -102,13 +102,14 @@ __device__ void clear_slot(MergeSmem<G, kSlots>& sm, int slot) {
   }
 }
 
-// Merge the slots and write this split's partial records
+// Merge slots 0 .. kUse-1 and write this split's partial records
 // partials[(partial_base + hh * splits + split) * 132] = (m, l, -, -, acc[128]).
-// Must be reached by all threads of the block after the slots are written
-// (with a barrier first unless the caller has just passed one: kSync).
-// The records of all splits are merged by merge_splits_kernel, launched
-// after the decode kernel on the same stream.
-template <int G, int kSlots, bool kSync = true>
+// Slots from kUse on must be empty (leaving them out changes nothing: an
+// empty slot has weight 0).  Must be reached by all threads of the block
+// after the slots are written (with a barrier first unless the caller has
+// just passed one: kSync).  The records of all splits are merged by
+// merge_splits_kernel, launched after the decode kernel on the same stream.
+template <int G, int kSlots, bool kSync = true, int kUse = kSlots>
 __device__ void write_partial(MergeSmem<G, kSlots>& sm, float* partials, size_t partial_base, int split,
                               int splits) {
   const int tid = threadIdx.x;
@@ -116,17 +117,18 @@ __device__ void write_partial(MergeSmem<G, kSlots>& sm, float* partials, size_t 
   for (int i = tid; i < G * kHeadDim; i += blockDim.x) {
     const int hh = i / kHeadDim;
     const int d = i % kHeadDim;
-    float m[kSlots];
+    static_assert(kUse <= kSlots, "merging more slots than there are");
+    float m[kUse];
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kSlots; ++w) {
+    for (int w = 0; w < kUse; ++w) {
       m[w] = sm.m[w][hh];
       M = fmaxf(M, m[w]);
     }
     float Lsum = 0.f, A = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kSlots; ++w) {
+      for (int w = 0; w < kUse; ++w) {
         const float f = fast_exp2(m[w] - M);   // 0 for an empty slot (m = -inf)
         Lsum = fmaf(sm.l[w][hh], f, Lsum);
         A = fmaf(sm.acc[w][hh][d], f, A);

@@ -43,33 +43,35 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 // After the spread (spread_codes) the code at bit position 2r of its byte
-// carries the weight 4^r (masks 0x03, 0x0C, 0x30, 0xC0); the other operand
-// is multiplied by 64 / 4^r so that every code ends up with weight 64.
-__device__ constexpr float kFac[4] = {64.f, 16.f, 4.f, 1.f};
+// carries the weight 4^r (masks 0x03, 0x0C, 0x30); the other operand is
+// multiplied by 64 / 4^r so that every code ends up with weight 64.  The top
+// field is stored as 64 - 64 c (so that it fits int8) and its operand is
+// negated: (-x) (64 - 64 c) = 64 x c - 64 x, the -64 x being cancelled by
+// the accumulator's start value.
+__device__ constexpr float kFac[4] = {64.f, 16.f, 4.f, -1.f};
 
 // 16 packed codes (bits 2k..2k+1 = code k) -> 16 int8 lanes of an MFMA
-// operand.  Byte b of output dword r holds code 4b + r times 4^r; the top
-// field is flipped into int8 range, 64 * code - 128, and the -128 is
-// cancelled by the accumulator's start value (field3_bias).
+// operand.  Byte b of output dword r holds code 4b + r times 4^r for r < 3;
+// the top field holds 64 - 64 * code (one XOR turns 64 c into it), paired
+// with a negated operand and the start value of field3_bias.
 __device__ __forceinline__ v4i spread_codes(uint32_t x) {
   v4i o;
   o[0] = static_cast<int>(x & 0x03030303u);
   o[1] = static_cast<int>(x & 0x0C0C0C0Cu);
   o[2] = static_cast<int>(x & 0x30303030u);
-  o[3] = static_cast<int>((x & 0xC0C0C0C0u) ^ 0x80808080u);
+  o[3] = static_cast<int>((x & 0xC0C0C0C0u) ^ 0x40404040u);
   return o;
 }
 
-// 128 * (sum of the A operand over the K positions that carry top-field
-// codes), the start value that cancels the -128 offset of spread_codes in a
-// two-step (K = 128) product with A halves a0, a1.
+// -64 * (sum of the A operand over the K positions that carry top-field
+// codes): the start value of a two-step (K = 128) product with A halves a0,
+// a1 that removes the constant 64 of the top field, leaving -64 c times the
+// (negated) operand there.
 __device__ __forceinline__ v4i field3_bias(const v4i& a0, const v4i& a1) {
-  const v4i b64 = {0, 0, 0, 0x40404040};   // 64 at the top-field positions
+  const v4i bm64 = {0, 0, 0, static_cast<int>(0xC0C0C0C0u)};   // -64 at the top-field positions
   v4i c = {0, 0, 0, 0};
-  c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b64, c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b64, c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b64, c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b64, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bm64, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bm64, c, 0, 0, 0);
   return c;
 }
 
@@ -188,23 +190,45 @@ __device__ __forceinline__ void wait_groups_outstanding(int rem) {
   }
 }
 
-// Registers of the group being computed (see the lane roles above).
-__device__ __forceinline__ void read_stage(GroupBytes& r, const uint8_t* stage, int lane) {
+// Byte offsets inside a stage of the operands a lane reads (see the lane
+// roles above), fixed for the whole kernel, so that each read of a group is
+// one of these plus an immediate.  Key rows: token t = base + 4 b + c of
+// tile 4 c + b sits at half-row slot k_slot(t, gl / 2); since t / 16 = w and
+// bit 0 of t is c, that is byte 32 (base + 4 b + (c ^ (w & 1))) + 8 gl.
+struct StageLane {
+  int k[2];   // key codes of the tiles with c = 0, 1 (+ 128 b)
+  int v;      // value codes of channel n (+ 512 j)
+  int nrm;    // norms of tokens base + 4 b (+ 8 b)
+  int vsz;    // value (s, z) of tokens base + 4 b (+ 16 b)
+  int ksz;    // key (s, z) of channels base + 4 b (+ 16 b)
+};
+
+__device__ __forceinline__ StageLane stage_lane(int lane) {
   const int gl = lane >> 4;
   const int n = lane & 15;
+  const int w1 = (n >> 1) & 1;
   const int base = 16 * (n >> 1) + 2 * (n & 1);   // token / channel 16w + u
+  StageLane o;
+  o.k[0] = kStageK + 32 * (base + w1) + 8 * gl;
+  o.k[1] = kStageK + 32 * (base + 1 - w1) + 8 * gl;
+  o.v = kStageV + 32 * n + 8 * gl;
+  o.nrm = kStageNorm + 2 * base;
+  o.vsz = kStageVsz + 4 * base;
+  o.ksz = kStageKsz + 4 * base;
+  return o;
+}
+
+// Registers of the group being computed.
+__device__ __forceinline__ void read_stage(GroupBytes& r, const uint8_t* stage, const StageLane& o) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = base + 4 * (i & 3) + (i >> 2);
-    r.kd[i] = *reinterpret_cast<const uint2*>(stage + kStageK + 16 * k_slot(t, gl >> 1) + 8 * (gl & 1));
-  }
+  for (int i = 0; i < 8; ++i) r.kd[i] = *reinterpret_cast<const uint2*>(stage + o.k[i >> 2] + 128 * (i & 3));
 #pragma unroll
-  for (int j = 0; j < 8; ++j) r.vd[j] = *reinterpret_cast<const uint2*>(stage + kStageV + (16 * j + n) * 32 + 8 * gl);
+  for (int j = 0; j < 8; ++j) r.vd[j] = *reinterpret_cast<const uint2*>(stage + o.v + 512 * j);
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    r.nrm[b] = *reinterpret_cast<const uint32_t*>(stage + kStageNorm + 2 * (base + 4 * b));
-    r.vsz[b] = *reinterpret_cast<const uint2*>(stage + kStageVsz + 4 * (base + 4 * b));
-    r.ksz[b] = *reinterpret_cast<const uint2*>(stage + kStageKsz + 4 * (base + 4 * b));
+    r.nrm[b] = *reinterpret_cast<const uint32_t*>(stage + o.nrm + 8 * b);
+    r.vsz[b] = *reinterpret_cast<const uint2*>(stage + o.vsz + 16 * b);
+    r.ksz[b] = *reinterpret_cast<const uint2*>(stage + o.ksz + 16 * b);
   }
 }
 
@@ -495,7 +519,7 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: loop control in scalar registers
   const int lane = tid & 63;
   const int gl = lane >> 4;   // lane group: head of the row block / operand K slice
   const int n = lane & 15;
@@ -663,12 +687,13 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
     const int first_i = (simd < C::kLoaders) ? 1 : 0;                  // SIMD's first compute wave: simd + 4 first_i
     const int n_simd = (C::kWaves - 1 - simd) / 4 + 1 - first_i;      // compute waves on this SIMD
     GroupBytes cur;
+    const StageLane sl = stage_lane(lane);
     for (int k = simd + 4 * (wave / 4 - first_i); k < n_k; k += 4 * n_simd) {
       const int s = k % C::kRing;
       const int use = k / C::kRing;
       while (__hip_atomic_load(&sm.filled[s], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <= use)
         __builtin_amdgcn_s_sleep(1);
-      read_stage(cur, sm.ring[s], lane);
+      read_stage(cur, sm.ring[s], sl);
       // the stage may be refilled once every lane's reads have returned
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __hip_atomic_store(&sm.emptied[s], use + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -699,7 +724,13 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
   __syncthreads();
 
   const size_t partial_base = (static_cast<size_t>(b) * a.num_q_heads + qh0) * a.splits;
-  write_partial<G, C::kSlots, false>(sm.merge, a.partials, partial_base, split, a.splits);
+  // the two bf16-tail slots hold tokens only in the workgroup that owns the
+  // tail group; elsewhere they are empty and left out of the merge
+  const int g_tail = nq / kGroup;
+  if (nt > 0 && g_tail < n_groups && g_tail % S == split)
+    write_partial<G, C::kSlots, false>(sm.merge, a.partials, partial_base, split, a.splits);
+  else
+    write_partial<G, C::kSlots, false, C::kCompute>(sm.merge, a.partials, partial_base, split, a.splits);
 }
 
 template <int G>

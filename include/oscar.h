@@ -54,6 +54,14 @@
  *                               (after the rotation, which keeps it).
  *  - k_tail, v_tail : bf16 [batch][num_kv_heads][128][128]; the tokens of
  *              the current, not yet complete group (at most 127 are read).
+ *  Paged cache (block_table != NULL): the blocks live in a pool of pages,
+ *  blocks : uint8 [num_pages][num_kv_heads][OSCAR_BLOCK_BYTES], one page per
+ *  group of 128 tokens holding that group's block for every KV head; group g
+ *  of sequence b is page block_table[b * (capacity/128) + g].  Pages may be
+ *  assigned in any order; two groups written by the same call must not share
+ *  a page.  The kernels clamp a table entry to [0, num_pages) before using
+ *  it, so a stale entry reaches some page of the pool, never memory outside
+ *  it.
  *  Dequantization: key (rotated domain) = n * (s * c + z) with the group's
  *  (s, z) for that channel; value = s * c + z with the token's (s, z).
  *  blocks must be 256-byte aligned (every block then is), the tails
@@ -69,7 +77,7 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 2
+#define OSCAR_ABI_VERSION 3
 #define OSCAR_HEAD_DIM 128
 #define OSCAR_GROUP 128
 
@@ -103,9 +111,16 @@ typedef struct oscar_kv_cache {
   int32_t group;           /* must be 128 */
   int32_t capacity;        /* tokens per sequence; a positive multiple of 128 */
   int32_t flags;           /* OSCAR_KEYS_* bits; the quantizer and the decode of a cache must agree */
-  uint8_t* blocks;          /* [batch][num_kv_heads][capacity/128][OSCAR_BLOCK_BYTES] */
+  uint8_t* blocks;          /* [batch][num_kv_heads][capacity/128][OSCAR_BLOCK_BYTES], or the page pool */
   uint16_t* k_tail;        /* read by the decode calls, written by oscar_decode_attn_append only; */
   uint16_t* v_tail;        /* may be NULL if no tail is ever used */
+  /* Paged layout (a block table as in paged-attention serving): NULL for the
+   * contiguous layout above; else device int32 [batch][capacity/128], the
+   * page of each group (4-byte aligned), and blocks is the pool of
+   * num_pages pages (see the layout above). */
+  const int32_t* block_table;
+  int32_t num_pages;       /* pages in the pool (> 0) when block_table is set; ignored otherwise */
+  int32_t reserved;        /* must be 0 */
 } oscar_kv_cache;
 
 /* Version of this ABI (OSCAR_ABI_VERSION). */

@@ -46,6 +46,9 @@ class KVCacheDesc(ctypes.Structure):
         ("blocks", ctypes.c_void_p),
         ("k_tail", ctypes.c_void_p),
         ("v_tail", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -144,20 +147,51 @@ class PackedCache:
       k_norm  int16 [B,H,G,128] (fp16)
     fp16 data is viewed as int16 so that the bit patterns are exact.
     k_tail / v_tail are bf16 [B,H,128,128].
+
+    Paged layout (``num_pages`` given): ``blocks`` is a pool uint8
+    [num_pages, H, 9472], one page per group for all KV heads, and
+    ``block_table`` int32 [B, C/128] (on the device) names the page of each
+    group.  The default table gives sequence b's groups the pages
+    b * C/128 + g; any table whose entries are pages of the pool works.
     """
 
-    def __init__(self, batch: int, num_kv_heads: int, capacity: int, device="cuda", flags: int = 0):
+    def __init__(self, batch: int, num_kv_heads: int, capacity: int, device="cuda", flags: int = 0,
+                 num_pages: Optional[int] = None, block_table: Optional[torch.Tensor] = None):
         if capacity % GROUP:
             raise ValueError("capacity must be a multiple of 128")
         B, H, C = batch, num_kv_heads, capacity
         dev = torch.device(device)
         self.batch, self.num_kv_heads, self.capacity = B, H, C
         self.flags = int(flags)   # KEYS_UNROTATED | KEYS_UNSCALED; 0 = OScaR
-        self.blocks = torch.zeros((B, H, C // GROUP, BLOCK_BYTES), dtype=torch.uint8, device=dev)
+        self.num_pages = None if num_pages is None else int(num_pages)
+        self.block_table = None
+        if self.num_pages is None:
+            if block_table is not None:
+                raise ValueError("a block table needs num_pages")
+            self.blocks = torch.zeros((B, H, C // GROUP, BLOCK_BYTES), dtype=torch.uint8, device=dev)
+        else:
+            if self.num_pages <= 0:
+                raise ValueError("num_pages must be positive")
+            self.blocks = torch.zeros((self.num_pages, H, BLOCK_BYTES), dtype=torch.uint8, device=dev)
+            if block_table is None:
+                block_table = torch.arange(B * (C // GROUP), dtype=torch.int32).remainder(self.num_pages)
+            block_table = block_table.to(device=dev, dtype=torch.int32).contiguous()
+            if tuple(block_table.shape) != (B, C // GROUP):
+                raise ValueError("block_table must be [batch, capacity / 128]")
+            self.block_table = block_table
         self.k_tail = torch.zeros((B, H, GROUP, HEAD_DIM), dtype=torch.bfloat16, device=dev)
         self.v_tail = torch.zeros((B, H, GROUP, HEAD_DIM), dtype=torch.bfloat16, device=dev)
 
+    def group_blocks(self) -> torch.Tensor:
+        """The blocks as [B, H, C/128, 9472] (for a paged cache, gathered
+        through the block table: a copy)."""
+        if self.block_table is None:
+            return self.blocks
+        return self.blocks[self.block_table.long()].permute(0, 2, 1, 3)
+
     def _part(self, off: int, nbytes: int, dtype, shape):
+        if self.block_table is not None:
+            raise ValueError("field views exist for the contiguous layout only (see group_blocks)")
         v = self.blocks[..., off:off + nbytes]
         if dtype is not torch.uint8:
             v = v.view(dtype)
@@ -189,7 +223,8 @@ class PackedCache:
             raise ValueError("blocks must be 256-byte aligned")
         return KVCacheDesc(
             self.batch, self.num_kv_heads, HEAD_DIM, GROUP, self.capacity, self.flags, blocks,
-            _ptr(self.k_tail, torch.bfloat16, "k_tail"), _ptr(self.v_tail, torch.bfloat16, "v_tail"))
+            _ptr(self.k_tail, torch.bfloat16, "k_tail"), _ptr(self.v_tail, torch.bfloat16, "v_tail"),
+            _ptr(self.block_table, torch.int32, "block_table"), self.num_pages or 0, 0)
 
     def nbytes_packed(self) -> int:
         """Bytes of the packed representation (codes, scales, zero-points, norms)."""

@@ -124,6 +124,12 @@ oscar_status check_cache(const char* fn, const oscar_kv_cache* c) {
     return fail(OSCAR_EINVAL, "%s: cache->blocks is not 256-byte aligned", fn);
   if ((c->k_tail && !aligned16(c->k_tail)) || (c->v_tail && !aligned16(c->v_tail)))
     return fail(OSCAR_EINVAL, "%s: tail buffers must be 16-byte aligned", fn);
+  if (c->reserved != 0) return fail(OSCAR_EINVAL, "%s: cache->reserved must be 0", fn);
+  if (c->block_table) {
+    if ((reinterpret_cast<uintptr_t>(c->block_table) & 3u) != 0)
+      return fail(OSCAR_EINVAL, "%s: cache->block_table is not 4-byte aligned", fn);
+    if (c->num_pages <= 0) return fail(OSCAR_EINVAL, "%s: a paged cache needs num_pages > 0 (got %d)", fn, c->num_pages);
+  }
   return OSCAR_OK;
 }
 
@@ -171,6 +177,8 @@ oscar_status oscar_quantize_kv(const oscar_kv_cache* cache, const uint16_t* k_sr
   if ((st = check_device(fn)) != OSCAR_OK) return st;
   QuantizeArgs a;
   a.blocks = cache->blocks;
+  a.block_table = cache->block_table;
+  a.num_pages = cache->block_table ? cache->num_pages : 0;
   a.k_src = k_src;
   a.v_src = v_src;
   a.sb = src_stride_b;
@@ -218,6 +226,8 @@ oscar_status decode_int2_splits(const char* fn, const oscar_kv_cache* cache, con
   const SplitPlan p = plan_int2(cache->batch, cache->num_kv_heads, max_tokens);
   DecodeInt2Args a;
   a.blocks = cache->blocks;
+  a.block_table = cache->block_table;
+  a.num_pages = cache->block_table ? cache->num_pages : 0;
   a.k_tail = cache->k_tail;
   a.v_tail = cache->v_tail;
   a.k_new = k_new;

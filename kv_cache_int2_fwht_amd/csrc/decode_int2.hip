@@ -159,10 +159,8 @@ __device__ __forceinline__ void lds_load16(const void* gptr, const uint8_t* lds)
                : "memory");
 }
 
-// The kDmaPerGroup loads that copy group g of a slice into a stage.
-__device__ __forceinline__ void dma_group(uint8_t* stage, const DecodeInt2Args& a, size_t slice, int groups_cap,
-                                          int g, int lane) {
-  const uint8_t* blk = a.blocks + (slice * groups_cap + g) * static_cast<size_t>(kStageBytes);
+// The kDmaPerGroup loads that copy the group block at blk into a stage.
+__device__ __forceinline__ void dma_group(uint8_t* stage, const uint8_t* blk, int lane) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int sl = 64 * j + lane;                       // stage slot this lane fills
@@ -554,6 +552,11 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
   if (tid == 0) sm.q_ready = 0;
   __syncthreads();
 
+  // block of the split's k-th group (a table lookup for a paged cache)
+  auto group_block = [&](int k) {
+    return a.blocks + group_block_index(a.block_table, a.num_pages, groups_cap, a.num_kv_heads, b, h, split + k * S) *
+                          static_cast<size_t>(kStageBytes);
+  };
   int issued = 0;   // groups this loader has requested, in order (its j-th is k = wave + j kLoaders)
   if (loader) {
     static_assert(C::kAhead * C::kLoaders <= C::kRing, "the first groups go to unused stages");
@@ -561,7 +564,7 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
     for (int j = 0; j < C::kAhead; ++j) {
       const int k = wave + j * C::kLoaders;
       if (split + k * S >= groups_cap) break;
-      dma_group(sm.ring[k % C::kRing], a, slice, groups_cap, split + k * S, lane);
+      dma_group(sm.ring[k % C::kRing], group_block(k), lane);
       ++issued;
     }
   }
@@ -601,14 +604,19 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
     // wave's in-order vector-memory counter shows when only the loads of
     // later groups are outstanding.
     const int n_mine = (n_k > wave) ? (n_k - wave + C::kLoaders - 1) / C::kLoaders : 0;
+    // the block of the next group to request, looked up one request ahead
+    // (a paged cache's table entry is then read long before it is needed)
+    const uint8_t* next_blk = (issued < n_mine) ? group_block(wave + issued * C::kLoaders) : a.blocks;
     for (int j = 0; j < n_mine; ++j) {
       for (; issued < min(j + C::kAhead, n_mine); ++issued) {
         const int k = wave + issued * C::kLoaders;
         const int s = k % C::kRing;
         const int use = k / C::kRing;   // earlier occupants of the stage
+        const uint8_t* blk = next_blk;
+        if (issued + 1 < n_mine) next_blk = group_block(k + C::kLoaders);
         while (__hip_atomic_load(&sm.emptied[s], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < use)
           __builtin_amdgcn_s_sleep(1);
-        dma_group(sm.ring[s], a, slice, groups_cap, split + k * S, lane);
+        dma_group(sm.ring[s], blk, lane);
       }
       // the counter wait is the release: the copies are in LDS before the
       // flag store issues (a release store would wait for every load)

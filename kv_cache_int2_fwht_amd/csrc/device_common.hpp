@@ -18,6 +18,21 @@ constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]: partner lane ^ 2
 constexpr int kDppRowRor4 = 0x124;  // rotate right by 4 within a 16-lane row
 constexpr int kDppRowRor8 = 0x128;  // rotate right by 8 within a 16-lane row
 
+// Index, in blocks of 9472 bytes, of the block of group g of KV head h of
+// sequence b.  Contiguous cache: blocks [batch][heads][groups_cap].  Paged
+// cache: page table[b * groups_cap + g] of a pool [pages][heads], the entry
+// clamped to [0, num_pages) so that any entry stays inside the pool.  The
+// callers pass uniform b, h and g, and the table is read-only for the whole
+// launch, so the entry is read with a scalar load.
+typedef __attribute__((address_space(4))) const int32_t* ConstI32Ptr;
+__device__ __forceinline__ size_t group_block_index(const int32_t* table, int32_t num_pages, int groups_cap,
+                                                    int num_kv_heads, int b, int h, int g) {
+  if (table == nullptr) return (static_cast<size_t>(b) * num_kv_heads + h) * groups_cap + g;
+  int page = ((ConstI32Ptr)(table))[static_cast<size_t>(b) * groups_cap + g];
+  page = min(max(page, 0), num_pages - 1);
+  return static_cast<size_t>(page) * num_kv_heads + h;
+}
+
 template <int kCtrl>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, true));

@@ -34,6 +34,8 @@ struct QuantizeArgs {
   int64_t sb, sh, st;
   const int32_t* dst_group_start;
   const int32_t* num_groups;
+  const int32_t* block_table;   // paged cache: page of each (sequence, group); nullptr = contiguous
+  int32_t num_pages;
   int32_t num_kv_heads;
   int32_t capacity;
   int32_t flags;   // OSCAR_KEYS_*
@@ -41,6 +43,8 @@ struct QuantizeArgs {
 
 struct DecodeInt2Args {
   const uint8_t* blocks;
+  const int32_t* block_table;   // paged cache: page of each (sequence, group); nullptr = contiguous
+  int32_t num_pages;
   uint16_t* k_tail;        // written only when a token is appended (k_new given)
   uint16_t* v_tail;
   const uint16_t* k_new;   // token appended to the tail in this launch ([B][Hkv][128]), or null

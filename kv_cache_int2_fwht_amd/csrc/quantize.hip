@@ -114,8 +114,9 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
   const int lane = tid & 63;
   const bool rotate = (a.flags & OSCAR_KEYS_UNROTATED) == 0;
   const bool scale = (a.flags & OSCAR_KEYS_UNSCALED) == 0;
-  const size_t slice = static_cast<size_t>(b) * a.num_kv_heads + h;
-  uint8_t* const blk = a.blocks + (slice * groups_cap + dst) * OSCAR_BLOCK_BYTES;   // this group's block
+  // this group's block (through the block table for a paged cache)
+  uint8_t* const blk =
+      a.blocks + group_block_index(a.block_table, a.num_pages, groups_cap, a.num_kv_heads, b, h, dst) * OSCAR_BLOCK_BYTES;
   const uint16_t* ksrc = a.k_src + b * a.sb + h * a.sh + static_cast<int64_t>(j) * kGroup * a.st;
   const uint16_t* vsrc = a.v_src + b * a.sb + h * a.sh + static_cast<int64_t>(j) * kGroup * a.st;
 

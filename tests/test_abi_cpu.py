@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert ob.abi_version() == 2
+    assert ob.abi_version() == 3
     assert ob.status_string(0) == "ok"
     assert ob.status_string(3) == "workspace too small"
     assert ob.status_string(99) == "unknown status"
@@ -69,7 +69,7 @@ needs_no_gpu = pytest.mark.skipif(not _no_gpu(), reason="placeholder pointers ar
 
 def _desc(**kw):
     d = dict(batch=1, num_kv_heads=8, head_dim=128, group=128, capacity=1024, flags=0,
-             blocks=0x10000, k_tail=0x60000, v_tail=0x70000)
+             blocks=0x10000, k_tail=0x60000, v_tail=0x70000, block_table=0, num_pages=0, reserved=0)
     d.update(kw)
     return ob.KVCacheDesc(*[d[f] for f, _ in ob.KVCacheDesc._fields_])
 
@@ -115,6 +115,31 @@ def test_decode_validation_errors():
     assert _decode(_desc(), ws_bytes=64) == ob.OSCAR_EWORKSPACE
     assert b"workspace" in L.oscar_last_error()
     assert _decode(_desc(), q=0x80004) == ob.OSCAR_EINVAL
+
+
+def test_cache_descriptor_mirrors_the_header():
+    """The ctypes mirror has the fields of struct oscar_kv_cache, in order."""
+    import re
+    text = open(os.path.join(ROOT, "include", "oscar.h")).read()
+    body = re.search(r"typedef struct oscar_kv_cache \{(.*?)\} oscar_kv_cache;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = re.findall(r"(\w+)\s*;", body)
+    assert names == [f for f, _ in ob.KVCacheDesc._fields_]
+    assert ctypes.sizeof(ob.KVCacheDesc) == 6 * 4 + 3 * 8 + 8 + 2 * 4
+
+
+@needs_no_gpu
+def test_paged_descriptor_validation():
+    L = ob.lib()
+    assert _decode(_desc(block_table=0x50000, num_pages=0)) == ob.OSCAR_EINVAL    # a pool needs pages
+    assert b"num_pages" in L.oscar_last_error()
+    assert _decode(_desc(block_table=0x50002, num_pages=8)) == ob.OSCAR_EINVAL    # table not 4-byte aligned
+    assert _decode(_desc(reserved=1)) == ob.OSCAR_EINVAL
+    assert b"reserved" in L.oscar_last_error()
+    assert _decode(_desc(block_table=0x50000, num_pages=8)) == ob.OSCAR_EHIP       # valid, but no device here
+    q = L.oscar_quantize_kv(ctypes.byref(_desc(block_table=0x50000, num_pages=-1)), 0x80000, 0x90000, 0, 0, 128,
+                            0x100, 0x200, 1, None)
+    assert q == ob.OSCAR_EINVAL
 
 
 @needs_no_gpu

@@ -58,6 +58,9 @@ def parse():
     p.add_argument("--batch8", action="store_true",
                    help="batch 8 with jittered 96K-128K lengths (quantized groups plus bf16 tails): "
                         "decode tokens/s per layer and HBM GB/s, against the bf16 kernel")
+    p.add_argument("--paged", action="store_true",
+                   help="the 128K layer decoded from a paged cache (shuffled pages of a pool) against the "
+                        "contiguous cache (one JSON line instead of the benchmark line)")
     p.add_argument("--sweep", action="store_true",
                    help="context sweep 8K..128K at batch 1 and 8: INT2 and bf16 decode steps, speed-up and "
                         "cache footprint (one JSON line per configuration instead of the benchmark line)")
@@ -289,6 +292,78 @@ def batch8(args):
                       "bf16_us_per_step": round(bf16_us, 2),
                       "bf16_GBs": round(bf16_bytes / (bf16_us * 1e-6) / 1e9, 1),
                       "speedup_vs_bf16": round(bf16_us / int2_us, 3)}), flush=True)
+
+
+def paged(args):
+    """The 128K-token layer (batch 1, 32 query / 8 KV heads) decoded from a
+    paged cache: each copy's 1024 groups sit in randomly shuffled pages of a
+    pool with 64 spare pages.  The same data in the contiguous layout is timed
+    in alternating regions on the same device; 16 copies of each are cycled.
+    Reports both step times, their algorithmic GB/s, and whether the outputs
+    are bit-identical.  One JSON line."""
+    import numpy as np
+    import torch
+    import synthetic as syn
+    from kv_cache_int2_fwht_amd import binding as ob
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = syn.workload(3)
+    B, H, Hq, T = w.batch, w.num_kv_heads, w.num_q_heads, w.lengths[0]
+    sm = 1.0 / np.sqrt(128.0)
+    k_src = torch.empty((B, H, T, 128), dtype=torch.bfloat16, device=dev)
+    v_src = torch.empty((B, H, T, 128), dtype=torch.bfloat16, device=dev)
+    for h in range(H):
+        k_src[0, h] = torch.from_numpy(syn.keys_slice(w, 0, h).view(np.int16)).to(dev).view(torch.bfloat16)
+        v_src[0, h] = torch.from_numpy(syn.values_slice(w, 0, h).view(np.int16)).to(dev).view(torch.bfloat16)
+    q = torch.from_numpy(syn.query(w, 0).view(np.int16)).to(dev).view(torch.bfloat16)[None].contiguous()
+    gc = T // 128
+    i32 = lambda x: torch.tensor(x, dtype=torch.int32, device=dev)   # noqa: E731
+    base = ob.PackedCache(B, H, T, device=dev)
+    ob.quantize_kv(base, k_src, v_src, i32([0]), i32([gc]), gc)
+    n_copies = max(1, args.copies)
+    contig = [ob.PackedCache(B, H, T, device=dev) for _ in range(n_copies)]
+    for c in contig:
+        c.blocks.copy_(base.blocks)
+    pools = []
+    for i in range(n_copies):
+        table = np.random.default_rng([0x9A6E, i]).permutation(gc + 64)[:gc].astype(np.int32)[None]
+        pc = ob.PackedCache(B, H, T, device=dev, num_pages=gc + 64, block_table=torch.from_numpy(table))
+        pc.blocks[pc.block_table[0].long()] = base.blocks[0].permute(1, 0, 2)
+        pools.append(pc)
+    nq, nt = i32([T]), i32([0])
+    ws = ob.alloc_workspace(B, H, Hq, T, device=dev)
+    out_c = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    out_p = torch.empty_like(out_c)
+    stream = torch.cuda.current_stream()
+
+    def timed(caches, out, n):
+        for i in range(10):
+            ob.decode_attn(caches[i % len(caches)], nq, nt, T, q, sm, out, ws, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            ob.decode_attn(caches[i % len(caches)], nq, nt, T, q, sm, out, ws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    tc, tp = [], []
+    for _ in range(5):
+        tc.append(timed(contig, out_c, args.steps))
+        tp.append(timed(pools, out_p, args.steps))
+    ob.decode_attn(contig[0], nq, nt, T, q, sm, out_c, ws, stream=stream)
+    ob.decode_attn(pools[0], nq, nt, T, q, sm, out_p, ws, stream=stream)
+    torch.cuda.synchronize()
+    nbytes = B * H * T * BYTES_PER_TOKEN_HEAD + B * Hq * 128 * (2 + 4)
+    c_us, p_us = sorted(tc)[2], sorted(tp)[2]
+    print(json.dumps({"paged": "llama31-8b-layer-128k, 1024 groups in shuffled pages of a 1088-page pool",
+                      "contiguous_us_per_step": round(c_us, 3), "paged_us_per_step": round(p_us, 3),
+                      "contiguous_GBs": round(nbytes / (c_us * 1e-6) / 1e9, 1),
+                      "paged_GBs": round(nbytes / (p_us * 1e-6) / 1e9, 1),
+                      "regions_us": {"contiguous": [round(x, 3) for x in tc], "paged": [round(x, 3) for x in tp]},
+                      "bit_identical": bool(torch.equal(out_c, out_p))}), flush=True)
 
 
 def append_loop(args):
@@ -539,6 +614,9 @@ def main():
         return
     if args.batch8:
         batch8(args)
+        return
+    if args.paged:
+        paged(args)
         return
 
     import numpy as np

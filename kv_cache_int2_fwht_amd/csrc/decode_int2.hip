@@ -13,18 +13,23 @@
 // Both contractions over the codes run on the matrix cores as exact integer
 // products (v_mfma_i32_16x16x64_i8): the 2-bit codes are spread to int8 with
 // one mask per four codes (the code's bit position becomes a power-of-two
-// weight 1, 4 or 16 that is divided out of the other operand), and the fp32
-// operand (q' for the scores, p * vs for the values) is written as a 32-bit
-// fixed-point integer with a per-group power-of-two scale and split into four
-// signed base-256 digits, one matrix row per (head, digit).  The int32 results
-// are recombined exactly and scaled back, so the only rounding is the 2^-26
-// relative fixed-point step of q' and p * vs.
+// weight 1, 4 or 16, divided out of the other operand; the top field is
+// stored as 64 - 64 c against a negated operand), and the fp32 operand (q'
+// for the scores, p * vs for the values) is written as a 32-bit fixed-point
+// integer with a per-group power-of-two scale and split into four signed
+// base-256 digits, one matrix row per (head, digit).  The int32 results are
+// recombined exactly and scaled back, so the only rounding is the
+// fixed-point step of q' and p * vs (2^-24 of the group's largest value)
+// and fp32 rounding.
 //
-// Work split: grid (split, KV head, sequence); one 8-wave workgroup per
-// compute unit; the waves claim the split's 128-token groups one at a time
-// (prefetching the next group's bytes while computing the current one) and
-// keep a base-2 online softmax each.  Lane
-// roles inside a wave (lane = 16 * r + n, w = n >> 1, u = 2 (n & 1)):
+// Work split: grid (split, KV head, sequence), about one workgroup per
+// compute unit, all resident at once; split s owns the groups s, s + S, ...
+// Inside a workgroup two loader waves stream the groups' blocks into an LDS
+// ring with direct global -> LDS copies, and the compute waves take the
+// groups in a fixed round-robin over the SIMDs, each keeping a base-2 online
+// softmax (a fixed assignment keeps the summation order, so results repeat
+// bit for bit).  Lane roles inside a compute wave (lane = 16 * r + n,
+// w = n >> 1, u = 2 (n & 1)):
 //  * score / softmax lane (r, n): head r of the row block, the tokens
 //    16w + 4b + u + c of the group (b = 0..3, c = 0..1; column n of tile
 //    4c + b);
@@ -33,8 +38,8 @@
 // With these sets, the four digits of the values a lane owns for one c land
 // in four consecutive bytes of one MFMA operand row, so each lane stages
 // its operand bytes with one 8-byte LDS write per digit row.
-// The waves merge in LDS into one partial record per split; merge.hip
-// combines the splits.
+// The compute waves' states (and the bf16 tail's) merge in LDS into one
+// partial record per split; merge.hip combines the splits.
 #include "decode_common.hpp"
 
 namespace oscar {

@@ -69,17 +69,23 @@ __device__ __forceinline__ void key_fwht(const uint16_t* row, int L, bool rotate
       }
     }
   }
+  // across the quad: x + partner, or partner - x, as one fused multiply-add
+  // with a factor of +-1 (the product is exact, so it rounds like the sum)
+  const double s1 = (L & 1) ? -1.0 : 1.0;
+  const double s2 = (L & 2) ? -1.0 : 1.0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = fma(s1, x[i], dpp_f64<kDppQuadXor1>(x[i]));
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const double p = dpp_f64<kDppQuadXor1>(x[i]);
-    x[i] = (L & 1) ? (p - x[i]) : (x[i] + p);
-  }
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const double p = dpp_f64<kDppQuadXor2>(x[i]);
-    x[i] = (L & 2) ? (p - x[i]) : (x[i] + p);
+    x[i] = fma(s2, x[i], dpp_f64<kDppQuadXor2>(x[i]));
   }
 }
+
+// Per-channel LDS arrays are read and written by the four lanes of a quad
+// at channels 32 L + i (L = 0..3), 256 bytes apart: one bank.  One padding
+// entry after every 32 channels puts the four lanes on four different banks.
+constexpr int kChPadded = kHeadDim + kHeadDim / 32;
+__device__ __forceinline__ int padc(int c) { return c + (c >> 5); }
 
 struct QuantSmem {
   // The group's block is assembled here and written out at the end in whole
@@ -88,13 +94,13 @@ struct QuantSmem {
   // `out_params`.
   union alignas(16) {
     struct {
-      double red_min[16][kHeadDim];   // per-channel min / max of the scaled keys, one row per (wave, 16-lane row)
-      double red_max[16][kHeadDim];
+      double red_min[16][kChPadded];   // per-channel min / max of the scaled keys, one row per (wave, 16-lane row)
+      double red_max[16][kChPadded];
     } r;
     uint8_t out_codes[OSCAR_BLOCK_K_SZ];                        // key codes, then value codes
   } u;
   alignas(16) uint8_t out_params[OSCAR_BLOCK_BYTES - OSCAR_BLOCK_K_SZ];   // key (s, z), value (s, z), key norms
-  double zs[kHeadDim], ss[kHeadDim], inv_s[kHeadDim];   // key (z16, s16, 1 / s16) per channel
+  double zs[kChPadded], ss[kChPadded], inv_s[kChPadded];   // key (z16, s16, 1 / s16) per channel (padc index)
   double inv_n[kGroup];                                  // 1 / (sqrt(128) n16) per token (0 if n16 = 0)
   double vz[kGroup], vs[kGroup], vinv[kGroup];           // value (z16, s16, 1 / s16) per token
   uint4 vrow[kGroup][kHeadDim / 8];                      // the group's values (bf16)
@@ -128,11 +134,19 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
   const int L = lane & 3;
   const int slot = lane >> 2;
   const int row = wave * 4 + (lane >> 4);
+  // the first pass's transformed keys stay in registers until their codes
+  // are decided after the block-wide reduction (the second pass's are
+  // transformed again then: keeping both would not fit the registers)
+  double xk[32];
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
     const int t = wave * 32 + pass * 16 + slot;
     double x[32];
     key_fwht(ksrc + static_cast<int64_t>(t) * a.st, L, rotate, x);
+    if (pass == 0) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) xk[i] = x[i];
+    }
     // ||y||^2 = sum(Y^2) / 128 for the unnormalised transform Y = sqrt(128) y
     // (sum(k^2) when the rotation is off).
     double ssq = 0.0;
@@ -159,11 +173,11 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
       mx = fmax(mx, dpp_f64<kDppRowRor8>(mx));
       if ((lane & 15) < 4) {
         if (pass == 0) {
-          sm.u.r.red_min[row][32 * L + i] = mn;
-          sm.u.r.red_max[row][32 * L + i] = mx;
+          sm.u.r.red_min[row][padc(32 * L + i)] = mn;
+          sm.u.r.red_max[row][padc(32 * L + i)] = mx;
         } else {   // the same lane wrote these entries in the first pass
-          sm.u.r.red_min[row][32 * L + i] = fmin(sm.u.r.red_min[row][32 * L + i], mn);
-          sm.u.r.red_max[row][32 * L + i] = fmax(sm.u.r.red_max[row][32 * L + i], mx);
+          sm.u.r.red_min[row][padc(32 * L + i)] = fmin(sm.u.r.red_min[row][padc(32 * L + i)], mn);
+          sm.u.r.red_max[row][padc(32 * L + i)] = fmax(sm.u.r.red_max[row][padc(32 * L + i)], mx);
         }
       }
     }
@@ -211,20 +225,21 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
 
   // ---------------- key parameters per channel ----------------
   if (tid < kHeadDim) {
-    double lo = sm.u.r.red_min[0][tid], hi = sm.u.r.red_max[0][tid];
+    const int pt = padc(tid);
+    double lo = sm.u.r.red_min[0][pt], hi = sm.u.r.red_max[0][pt];
 #pragma unroll
     for (int r = 1; r < 16; ++r) {
-      lo = fmin(lo, sm.u.r.red_min[r][tid]);
-      hi = fmax(hi, sm.u.r.red_max[r][tid]);
+      lo = fmin(lo, sm.u.r.red_min[r][pt]);
+      hi = fmax(hi, sm.u.r.red_max[r][pt]);
     }
     const uint16_t s_bits = f64_to_f16_bits_rne_sat((hi - lo) / 3.0);
     const uint16_t z_bits = f64_to_f16_bits_rne_sat(lo);
     reinterpret_cast<uint32_t*>(sm.out_params)[tid] =
         static_cast<uint32_t>(s_bits) | (static_cast<uint32_t>(z_bits) << 16);
     const double s16 = f16_bits_to_f64(s_bits);
-    sm.zs[tid] = f16_bits_to_f64(z_bits);
-    sm.ss[tid] = s16;
-    sm.inv_s[tid] = (s16 > 0.0) ? 1.0 / s16 : 0.0;
+    sm.zs[pt] = f16_bits_to_f64(z_bits);
+    sm.ss[pt] = s16;
+    sm.inv_s[pt] = (s16 > 0.0) ? 1.0 / s16 : 0.0;
   }
 
   __syncthreads();   // the key ranges are read: their space now takes the codes
@@ -251,17 +266,22 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
   }
   __syncthreads();
 
-  // ---------------- keys, second pass: the same transform again, then codes ----------------
+  // ---------------- keys, second pass: codes (the second 16 tokens transformed again) ----------------
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
     const int t = wave * 32 + pass * 16 + slot;
     double x[32];
-    key_fwht(ksrc + static_cast<int64_t>(t) * a.st, L, rotate, x);   // bit-identical to the first pass
+    if (pass == 0) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = xk[i];
+    } else {
+      key_fwht(ksrc + static_cast<int64_t>(t) * a.st, L, rotate, x);   // bit-identical to the first pass
+    }
     const double inv = sm.inv_n[t];
     uint32_t w0 = 0, w1 = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int c0 = 32 * L + i, c1 = 32 * L + 16 + i;
+      const int c0 = padc(32 * L + i), c1 = padc(32 * L + 16 + i);
       w0 |= code_from(x[i] * inv, sm.zs[c0], sm.ss[c0], sm.inv_s[c0]) << (2 * i);
       w1 |= code_from(x[16 + i] * inv, sm.zs[c1], sm.ss[c1], sm.inv_s[c1]) << (2 * i);
     }

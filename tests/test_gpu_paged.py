@@ -183,3 +183,36 @@ def test_paged_decode_append_equals_contiguous(gpu_lib):
     for b in range(B):
         assert np.array_equal(got[b, :, :ng[b]], ref[b, :, :ng[b]])
     _say(f"  80 append steps bit-identical; groups now {ng}")
+
+
+def test_paged_128k_layer_equals_contiguous(gpu_lib):
+    """The 128K-token Llama-3.1-8B layer (8 KV heads, 32 query heads) in the
+    launch configuration the benchmark times: quantized straight into
+    shuffled pages of a larger pool it gives the contiguous cache's bytes,
+    and its decode output equals the contiguous decode bit for bit."""
+    from kv_cache_int2_fwht_amd import binding as ob
+    dev = torch.device("cuda:0")
+    w = syn.workload(3)
+    B, H, Hq, T = w.batch, w.num_kv_heads, w.num_q_heads, w.lengths[0]
+    _say(f"paged 128K layer: B={B} Hq={Hq} Hkv={H} T={T}")
+    k = torch.stack([bits_to_dev_bf16(syn.keys_slice(w, 0, h), dev) for h in range(H)])[None]
+    v = torch.stack([bits_to_dev_bf16(syn.values_slice(w, 0, h), dev) for h in range(H)])[None]
+    gc = T // 128
+    table = np.random.default_rng(7).permutation(gc + 64)[:gc].astype(np.int32)[None]
+    contig = ob.PackedCache(B, H, T, device=dev)
+    paged = ob.PackedCache(B, H, T, device=dev, num_pages=gc + 64, block_table=torch.from_numpy(table))
+    zero = torch.zeros(B, dtype=torch.int32, device=dev)
+    ng = torch.full((B,), gc, dtype=torch.int32, device=dev)
+    for c in (contig, paged):
+        ob.quantize_kv(c, k, v, zero, ng, gc)
+    torch.cuda.synchronize()
+    assert torch.equal(paged.group_blocks(), contig.blocks)
+    q = bits_to_dev_bf16(syn.query(w, 0), dev)[None].contiguous()
+    nq = torch.full((B,), T, dtype=torch.int32, device=dev)
+    outs = []
+    for c in (contig, paged):
+        out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+        ob.decode_attn(c, nq, zero, T, q, SM, out, ob.alloc_workspace(B, H, Hq, T, device=dev))
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])

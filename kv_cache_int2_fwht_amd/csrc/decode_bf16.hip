@@ -50,6 +50,14 @@ __device__ __forceinline__ const uint4* row_ptr(const uint16_t* base, size_t sli
   return reinterpret_cast<const uint4*>(base + (slice_row0 + min(t, last)) * kHeadDim) + c;
 }
 
+// 16 bytes of K or V with the nontemporal hint (the cache is read once per
+// step, as in the INT2 kernel's copies).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Maximum and sum over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48).
 __device__ __forceinline__ float max_over_rows(float x) {
   x = fmaxf(x, __shfl_xor(x, 16, kWave));
@@ -107,8 +115,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeBf16A
     const int t0 = step_t0(0);
 #pragma unroll
     for (int s2 = 0; s2 < kSteps; ++s2) {
-      cur.k[s2] = *row_ptr(a.k, row0, t0 + 4 * s2 + tq, last, c);
-      cur.v[s2] = *row_ptr(a.v, row0, t0 + 4 * s2 + tq, last, c);
+      cur.k[s2] = load_stream(row_ptr(a.k, row0, t0 + 4 * s2 + tq, last, c));
+      cur.v[s2] = load_stream(row_ptr(a.v, row0, t0 + 4 * s2 + tq, last, c));
     }
   }
   for (int i = 0; has_step(i); ++i) {
@@ -131,7 +139,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeBf16A
     const int t1 = step_t0(i + 1);
     if (more) {
 #pragma unroll
-      for (int s2 = 0; s2 < kSteps; ++s2) cur.k[s2] = *row_ptr(a.k, row0, t1 + 4 * s2 + tq, last, c);
+      for (int s2 = 0; s2 < kSteps; ++s2) cur.k[s2] = load_stream(row_ptr(a.k, row0, t1 + 4 * s2 + tq, last, c));
     }
     // ---- online softmax (base 2) over this step's tokens ----
     float p[G][kSteps];
@@ -170,7 +178,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeBf16A
     }
     if (more) {
 #pragma unroll
-      for (int s2 = 0; s2 < kSteps; ++s2) cur.v[s2] = *row_ptr(a.v, row0, t1 + 4 * s2 + tq, last, c);
+      for (int s2 = 0; s2 < kSteps; ++s2) cur.v[s2] = load_stream(row_ptr(a.v, row0, t1 + 4 * s2 + tq, last, c));
     }
   }
 

@@ -40,17 +40,17 @@ def _build(ob, w, dev, capacity=None):
     return cache, slices, kraw, vraw, q, lens, nq
 
 
-def _oracle_out(w, slices, q, lens):
+def _oracle_out(w, slices, q, lens, sm=SM):
     G = w.num_q_heads // w.num_kv_heads
     out = np.zeros((w.batch, w.num_q_heads, 128))
     for b in range(w.batch):
         for h in range(w.num_kv_heads):
             qq = syn.bf16_bits_to_f64(q[b, h * G:(h + 1) * G])
-            out[b, h * G:(h + 1) * G] = slices[b, h].decode(qq, SM)
+            out[b, h * G:(h + 1) * G] = slices[b, h].decode(qq, sm)
     return out
 
 
-def _run_int2(ob, cache, q, lens, nq, dev, max_tokens=None):
+def _run_int2(ob, cache, q, lens, nq, dev, max_tokens=None, sm=SM):
     B, Hq = q.shape[0], q.shape[1]
     mt = max(lens) if max_tokens is None else max_tokens
     qd = bits_to_dev_bf16(q, dev)
@@ -58,7 +58,7 @@ def _run_int2(ob, cache, q, lens, nq, dev, max_tokens=None):
     ws = ob.alloc_workspace(B, cache.num_kv_heads, Hq, mt, device=dev)
     ob.decode_attn(cache, torch.tensor(nq, dtype=torch.int32, device=dev),
                    torch.tensor([n - m for n, m in zip(lens, nq)], dtype=torch.int32, device=dev),
-                   mt, qd, SM, out, ws)
+                   mt, qd, sm, out, ws)
     torch.cuda.synchronize()
     return out.cpu().numpy(), ws
 
@@ -87,6 +87,39 @@ def test_int2_decode_matches_oracle(gpu_lib, case):
     got, _ = _run_int2(ob, cache, q, lens, nq, dev)
     err = assert_out_close(got, _oracle_out(w, slices, q, lens), case)
     _say(f"  max abs err {err:.2e}")
+
+
+@pytest.mark.parametrize("sm", [4.0, 1e-3])
+def test_int2_and_bf16_decode_sharp_and_flat_softmax(gpu_lib, sm):
+    """A softmax scale 45x the usual one (logits spread over hundreds of
+    units: the weights of most groups, and of whole early groups once a
+    later maximum appears, underflow to zero) and one 88x smaller (nearly
+    uniform weights, the output close to the mean value): both kernels stay
+    within the output tolerance of the oracle, quantized groups and bf16
+    tails alike."""
+    from kv_cache_int2_fwht_amd import binding as ob
+    dev = torch.device("cuda:0")
+    w = syn.custom_workload(2, 8, 2, [3000 + 40, 700], cfg_tag=150)
+    _say(f"int2/bf16 decode, sm_scale {sm}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} lens={w.lengths}")
+    cache, slices, kraw, vraw, q, lens, nq = _build(ob, w, dev)
+    got, _ = _run_int2(ob, cache, q, lens, nq, dev, sm=sm)
+    err = assert_out_close(got, _oracle_out(w, slices, q, lens, sm=sm), f"int2 sm {sm}")
+    B, H, Hq = w.batch, w.num_kv_heads, w.num_q_heads
+    G = Hq // H
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    ws = ob.alloc_workspace(B, H, Hq, max(lens), device=dev)
+    ob.decode_attn_bf16(bits_to_dev_bf16(kraw, dev), bits_to_dev_bf16(vraw, dev),
+                        torch.tensor(lens, dtype=torch.int32, device=dev), max(lens),
+                        bits_to_dev_bf16(q, dev), sm, out, ws)
+    torch.cuda.synchronize()
+    ref = np.zeros((B, Hq, 128))
+    for b in range(B):
+        for h in range(H):
+            ref[b, h * G:(h + 1) * G] = oracle.decode_bf16_slice(
+                syn.bf16_bits_to_f64(q[b, h * G:(h + 1) * G]), syn.bf16_bits_to_f64(kraw[b, h, :lens[b]]),
+                syn.bf16_bits_to_f64(vraw[b, h, :lens[b]]), sm)
+    err_bf = assert_out_close(out.cpu().numpy(), ref, f"bf16 sm {sm}")
+    _say(f"  max abs err int2 {err:.2e}, bf16 {err_bf:.2e}")
 
 
 def test_int2_decode_grid_larger_than_lengths(gpu_lib):

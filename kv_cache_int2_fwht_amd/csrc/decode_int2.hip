@@ -335,15 +335,19 @@ template <int G>
 struct Int2Cfg {
   static constexpr int kRB = (G + 3) / 4;  // 16-row blocks of (head, digit) rows
   static constexpr int kRows = kRB * 4;    // heads incl. zero padding
-  // One workgroup per compute unit: 12 waves (3 per SIMD) while the kernel
-  // fits in 168 VGPRs, 8 waves for 8 query heads per KV head.  The last
-  // kLoaders waves stream the cache into LDS; the others compute.
-  static constexpr int kWaves = (kRB == 1) ? 12 : 8;
+  // One workgroup per compute unit: 16 waves (4 per SIMD) while the kernel
+  // fits in 128 VGPRs, 8 waves for 8 query heads per KV head.  The first
+  // kLoaders waves stream the cache into LDS; the others compute.  Every
+  // SIMD spends about as long on its share of the groups as HBM takes to
+  // deliver them, and with 4 waves instead of 3 it hides more of each
+  // group's dependency stalls, so no backlog builds up on the two SIMDs
+  // that also run the loaders.
+  static constexpr int kWaves = (kRB == 1) ? 16 : 8;
   static constexpr int kLoaders = 2;
   static constexpr int kCompute = kWaves - kLoaders;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kSlots = kCompute + 2;  // one merge slot per compute wave + two for the bf16 tail
-  static constexpr int kRing = (kRB == 1) ? 10 : 8;   // group stages in LDS (a multiple of kLoaders)
+  static constexpr int kRing = 8;   // group stages in LDS (a multiple of kLoaders; 10 would not fit)
   static_assert(kWaves % 4 == 0 && kLoaders < 4, "compute waves on every SIMD");
   static constexpr int kAhead = 2;           // groups each loader has in flight (kAhead * kDmaPerGroup <= 63)
   static_assert(kRing % kLoaders == 0, "a stage is always refilled by the same loader");

@@ -716,6 +716,10 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
       // the stage may be refilled once every lane's reads have returned
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __hip_atomic_store(&sm.emptied[s], use + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      // The last group of each SIMD (one of the split's last four) lands when
+      // the stream ends and bounds the kernel's end, while the other waves
+      // on its SIMD finish groups that landed earlier: it is issued first.
+      if (k + 4 >= n_k) __builtin_amdgcn_s_setprio(2);
       const int g = split + k * S;
       float alpha[RB], inv_p[RB];
       score_phase<G>(cur, g * kGroup, total, qv, fac, sm, st, cw, gl, n, alpha, inv_p);

@@ -62,23 +62,39 @@ def key_errors(k, variant):
     return num / np.where(den > 0, den, 1.0)
 
 
+def softmax_weights(logits):
+    """Row-wise softmax of logits [G, N] (max subtracted), float64."""
+    x = np.asarray(logits, dtype=np.float64)
+    x = x - x.max(axis=-1, keepdims=True)
+    e = np.exp(x)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def tv_distance(p, p_hat):
+    """Total-variation distance per row of two weight vectors [G, N]:
+    1/2 sum_t |p_t - p_hat_t| (symmetric; 0 for equal weights, 1 for
+    weights on disjoint tokens)."""
+    return 0.5 * np.abs(np.asarray(p, np.float64) - np.asarray(p_hat, np.float64)).sum(axis=-1)
+
+
+def rel_output_error(out, ref):
+    """Relative error per row ||out - ref|| / ||ref||: the norm of the
+    reference (exact attention) is the denominator, not the estimate's."""
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return np.linalg.norm(out - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+
+
 def attention_tv(q, k, variant, sm_scale):
     """Max over query heads of the total-variation distance between the
     attention weights over the exact keys and over the variant's dequantized
-    keys: 1/2 sum_t |p_t - p_hat_t|.  Values do not enter, so the number
-    isolates the key quantizer."""
+    keys.  Values do not enter, so the number isolates the key quantizer."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     k_hat = quantize_dequantize_keys(k, variant)
-
-    def softmax(x):
-        x = x - x.max(axis=-1, keepdims=True)
-        e = np.exp(x)
-        return e / e.sum(axis=-1, keepdims=True)
-
-    p = softmax(sm_scale * q @ k.T)
-    p_hat = softmax(sm_scale * q @ k_hat.T)
-    return float(np.max(0.5 * np.abs(p - p_hat).sum(axis=-1)))
+    p = softmax_weights(sm_scale * q @ k.T)
+    p_hat = softmax_weights(sm_scale * q @ k_hat.T)
+    return float(np.max(tv_distance(p, p_hat)))
 
 
 def output_error(q, k, v, variant, sm_scale):
@@ -91,14 +107,15 @@ def output_error(q, k, v, variant, sm_scale):
     v_hat = dequant_values(vq["codes"], vq["vs16"], vq["vz16"])
     out = decode_bf16_slice(q, k_hat, v_hat, sm_scale)
     ref = decode_bf16_slice(q, k, v, sm_scale)
-    return float(np.max(np.linalg.norm(out - ref, axis=-1) / np.linalg.norm(ref, axis=-1)))
+    return float(np.max(rel_output_error(out, ref)))
 
 
 def study(workload=1, heads=(0, 1, 2, 3), sm_scale=1.0 / np.sqrt(128.0)):
     """Errors of every variant on the synthetic generator (sequence 0), as
-    means over the given KV heads."""
+    means over the given KV heads.  ``workload`` is a workload index or a
+    ``synthetic.Workload``; its quantized tokens (whole groups) are used."""
     import synthetic as syn
-    w = syn.workload(workload)
+    w = syn.workload(workload) if isinstance(workload, int) else workload
     G = w.num_q_heads // w.num_kv_heads
     n_quant = syn.split_lengths(w.total_tokens(0))[0]
     rows = {v: {"key_err_mean": [], "key_err_sink": [], "key_err_p99": [], "attn_tv": [], "out_err": []}

@@ -191,8 +191,11 @@ __device__ void bf16_tokens_wave(const uint16_t* k, const uint16_t* v, int n_tok
   const int n = lane & 15;    // operand row (query head) / result column (token of the tile)
   // every load first: the query (A operand: head n, zero rows beyond G,
   // channels 32 ks + 8 gl .. +7), the key rows of the tiles (B operand) and
-  // the value pairs of all tokens (lane = channel pair); tokens past n_tok
-  // read row 0 and are masked
+  // the value pairs of all tokens (lane = channel pair).  Tokens past n_tok
+  // read row 0 of the part and are discarded: their logits become -inf, and
+  // their value registers are set to 0, since the row may hold anything (a
+  // row past the tail that was never written, or the row into which another
+  // wave of this launch is storing the appended token) and 0 * NaN is NaN.
   uint4 qa[4], kb[kTiles][4];
   uint32_t vv[kTailPart];
   {
@@ -211,7 +214,8 @@ __device__ void bf16_tokens_wave(const uint16_t* k, const uint16_t* v, int n_tok
     for (int e = 0; e < kTailPart; ++e) {
       const uint16_t* vrow = (v_last != nullptr && e == last) ? v_last
                                                                : v + static_cast<size_t>(e < n_tok ? e : 0) * kHeadDim;
-      vv[e] = *reinterpret_cast<const uint32_t*>(vrow + 2 * lane);
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(vrow + 2 * lane);
+      vv[e] = (e < n_tok) ? x : 0u;
     }
   }
   // scores: tile j = tokens 16 j .. 16 j + 15; lane holds rows 4 gl + r of column n

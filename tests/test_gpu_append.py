@@ -93,3 +93,83 @@ def test_32k_append_inside_the_decode_launch(gpu_lib):
         sl = dataclasses.replace(pre, k_tail=k64[h, n_q0:n_q0 + 128], v_tail=v64[h, n_q0:n_q0 + 128])
         ref = sl.decode(syn.bf16_bits_to_f64(q[h * G:(h + 1) * G]), SM)
         assert_out_close(got[h * G:(h + 1) * G], ref, f"full tail, head {h}")
+
+
+@pytest.mark.parametrize("n_tail", [1, 64, 65, 127, 128])
+def test_append_with_non_finite_rows_past_the_tail(gpu_lib, n_tail):
+    """Tail rows past the appended token hold NaN (never written: the ABI does
+    not ask the caller to initialise them).  Each tail wave reads masked
+    tokens from a row of its own part, which at n_tail = 65 is the very row
+    the other wave stores the new token into; none of it may reach the
+    output.  Two sequences of 512 quantized tokens, two KV heads of four
+    query heads each, against the oracle."""
+    from kv_cache_int2_fwht_amd import binding as ob
+    from tests.helpers import upload_slice
+    dev = torch.device("cuda:0")
+    Hkv, Hq = 2, 8
+    G = Hq // Hkv
+    nq = 512
+    w = syn.custom_workload(2, Hq, Hkv, [nq + n_tail, nq + n_tail], cfg_tag=120 + n_tail)
+    print(f"append with NaN past the tail: n_tail {n_tail}", flush=True)
+    cache = ob.PackedCache(2, Hkv, nq + 128, device=dev)
+    refs, k_new, v_new = {}, [], []
+    for b in range(2):
+        kn, vn = [], []
+        for h in range(Hkv):
+            k64 = syn.bf16_bits_to_f64(syn.keys_slice(w, b, h))
+            v64 = syn.bf16_bits_to_f64(syn.values_slice(w, b, h))
+            s = oracle.quantize_slice(k64, v64, nq)
+            refs[b, h] = s
+            upload_slice(cache, b, h, dataclasses.replace(s, k_tail=s.k_tail[:n_tail - 1], v_tail=s.v_tail[:n_tail - 1]))
+            kn.append(syn.keys_slice(w, b, h)[nq + n_tail - 1])
+            vn.append(syn.values_slice(w, b, h)[nq + n_tail - 1])
+        k_new.append(np.stack(kn))
+        v_new.append(np.stack(vn))
+    nan = torch.tensor(float("nan"), dtype=torch.bfloat16, device=dev)
+    cache.k_tail[:, :, n_tail - 1:] = nan
+    cache.v_tail[:, :, n_tail - 1:] = nan
+    i32 = lambda x: torch.tensor(x, dtype=torch.int32, device=dev)   # noqa: E731
+    q_bits = np.stack([syn.query(w, b) for b in range(2)])
+    out = torch.empty((2, Hq, 128), dtype=torch.float32, device=dev)
+    ws = ob.alloc_workspace(2, Hkv, Hq, nq + 128, device=dev)
+    ob.decode_attn_append(cache, i32([nq, nq]), i32([n_tail, n_tail]), nq + n_tail,
+                          bits_to_dev_bf16(q_bits, dev), bits_to_dev_bf16(np.stack(k_new), dev),
+                          bits_to_dev_bf16(np.stack(v_new), dev), SM, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    for b in range(2):
+        for h in range(Hkv):
+            ref = refs[b, h].decode(syn.bf16_bits_to_f64(q_bits[b, h * G:(h + 1) * G]), SM)
+            assert_out_close(got[b, h * G:(h + 1) * G], ref, f"n_tail {n_tail}, sequence {b}, head {h}")
+    # the stored tail rows are exactly the appended tokens
+    np.testing.assert_array_equal(cache.k_tail[:, :, n_tail - 1].view(torch.int16).cpu().numpy().view(np.uint16),
+                                  np.stack(k_new))
+
+
+@pytest.mark.parametrize("n_tail", [1, 65])
+def test_decode_with_non_finite_rows_past_the_tail(gpu_lib, n_tail):
+    """oscar_decode_attn with NaN in every tail row at or past n_tail."""
+    from kv_cache_int2_fwht_amd import binding as ob
+    from tests.helpers import upload_slice
+    dev = torch.device("cuda:0")
+    Hkv, Hq, nq = 1, 4, 256
+    w = syn.custom_workload(1, Hq, Hkv, [nq + n_tail], cfg_tag=140 + n_tail)
+    print(f"decode with NaN past the tail: n_tail {n_tail}", flush=True)
+    k64 = syn.bf16_bits_to_f64(syn.keys_slice(w, 0, 0))
+    v64 = syn.bf16_bits_to_f64(syn.values_slice(w, 0, 0))
+    s = oracle.quantize_slice(k64, v64, nq)
+    cache = ob.PackedCache(1, Hkv, nq + 128, device=dev)
+    upload_slice(cache, 0, 0, s)
+    nan = torch.tensor(float("nan"), dtype=torch.bfloat16, device=dev)
+    cache.k_tail[:, :, n_tail:] = nan
+    cache.v_tail[:, :, n_tail:] = nan
+    i32 = lambda x: torch.tensor([x], dtype=torch.int32, device=dev)   # noqa: E731
+    q_bits = syn.query(w, 0)
+    out = torch.empty((1, Hq, 128), dtype=torch.float32, device=dev)
+    ws = ob.alloc_workspace(1, Hkv, Hq, nq + 128, device=dev)
+    ob.decode_attn(cache, i32(nq), i32(n_tail), nq + n_tail, bits_to_dev_bf16(q_bits[None], dev), SM, out, ws)
+    torch.cuda.synchronize()
+    got = out[0].cpu().numpy()
+    assert np.isfinite(got).all()
+    assert_out_close(got, s.decode(syn.bf16_bits_to_f64(q_bits), SM), f"n_tail {n_tail}")

@@ -271,6 +271,34 @@ oscar_status oscar_decode_merge(const float* partials, int32_t batch,
                                 float* out, void* stream);
 
 /*
+ * oscar_decode_attn_noalloc -- oscar_decode_attn without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * The split records live in a device array inside the library,
+ * OSCAR_NOALLOC_SCRATCH_BYTES large; every device the library runs on holds
+ * its own copy until the process ends.  The call allocates nothing and frees
+ * nothing.  Its first call on a device looks up that device's copy (the
+ * device current on the calling thread is the one used).  Arguments and
+ * result as in oscar_decode_attn.
+ *
+ * Limits: a shape whose records need more than OSCAR_NOALLOC_SCRATCH_BYTES
+ * (oscar_decode_workspace_bytes() > OSCAR_NOALLOC_SCRATCH_BYTES) is refused
+ * with OSCAR_EWORKSPACE before anything is launched.  Every call on a device
+ * shares that device's array: calls that may overlap on one device (on
+ * different streams, or from different threads without ordering) race and
+ * give wrong results; calls ordered on one stream are safe.  Every call
+ * writes all the records it reads, so nothing needs clearing between calls.
+ */
+#define OSCAR_NOALLOC_SCRATCH_BYTES (4 << 20)
+
+oscar_status oscar_decode_attn_noalloc(const oscar_kv_cache* cache,
+                                       const int32_t* n_quant, const int32_t* n_tail,
+                                       int32_t max_tokens, const uint16_t* q,
+                                       int32_t num_q_heads, float sm_scale, float* out,
+                                       void* stream);
+
+/*
  * oscar_decode_attn_bf16 -- the same decode step over unquantized bf16
  * keys and values: plain split-K flash-decoding, the counterpart of the
  * BF16 FlashDecoding-v2 baseline the pages compare against.

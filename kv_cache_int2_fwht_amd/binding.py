@@ -57,6 +57,7 @@ EXPORTED = (
     "oscar_quantize_kv", "oscar_decode_workspace_bytes",
     "oscar_decode_attn", "oscar_decode_attn_append", "oscar_decode_attn_bf16",
     "oscar_decode_num_splits", "oscar_decode_attn_splits", "oscar_decode_merge",
+    "oscar_decode_attn_noalloc",
 )
 
 
@@ -95,6 +96,8 @@ def lib():
     L.oscar_decode_num_splits.argtypes = [i32, i32, i32]
     L.oscar_decode_attn_splits.restype = ctypes.c_int
     L.oscar_decode_attn_splits.argtypes = [ctypes.POINTER(KVCacheDesc), vp, vp, i32, vp, i32, f32, vp, sz, vp]
+    L.oscar_decode_attn_noalloc.restype = ctypes.c_int
+    L.oscar_decode_attn_noalloc.argtypes = [ctypes.POINTER(KVCacheDesc), vp, vp, i32, vp, i32, f32, vp, vp]
     L.oscar_decode_merge.restype = ctypes.c_int
     L.oscar_decode_merge.argtypes = [vp, i32, i32, i32, vp, vp]
     _lib = L
@@ -356,3 +359,23 @@ def decode_merge(partials: torch.Tensor, out: torch.Tensor,
         raise ValueError("out must be [batch, q_heads, 128]")
     _check(lib().oscar_decode_merge(_ptr(partials, torch.float32, "partials"), B, Hq, S,
                                     _ptr(out, torch.float32, "out"), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 4 << 20   # OSCAR_NOALLOC_SCRATCH_BYTES
+
+
+def decode_attn_noalloc(cache: PackedCache, n_quant: torch.Tensor, n_tail: torch.Tensor, max_tokens: int,
+                        q: torch.Tensor, sm_scale: float, out: torch.Tensor,
+                        stream: Optional[torch.cuda.Stream] = None) -> None:
+    """oscar_decode_attn_noalloc: oscar_decode_attn with the split records in
+    the library's own device array (no workspace; calls on one device must
+    not overlap)."""
+    if q.dim() != 3 or q.shape[0] != cache.batch or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [batch, q_heads, 128]")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    d = cache.desc()
+    _check(lib().oscar_decode_attn_noalloc(ctypes.byref(d), _ptr(n_quant, torch.int32, "n_quant"),
+                                           _ptr(n_tail, torch.int32, "n_tail"), int(max_tokens),
+                                           _ptr(q, torch.bfloat16, "q"), q.shape[1], float(sm_scale),
+                                           _ptr(out, torch.float32, "out"), _stream(stream)))

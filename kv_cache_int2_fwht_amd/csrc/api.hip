@@ -133,6 +133,38 @@ oscar_status check_cache(const char* fn, const oscar_kv_cache* c) {
   return OSCAR_OK;
 }
 
+// Split records of oscar_decode_attn_noalloc: a file-scope device array, so
+// that the call needs no workspace from the caller.  In host code the name
+// `scratch` is only a stand-in for the symbol: host code uses the device
+// address that hipGetSymbolAddress returns for the current device (each
+// device holds its own copy of the array), never the name itself.
+static __device__ __align__(256) uint8_t scratch[OSCAR_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr with an error set if
+// the lookup fails.
+oscar_status scratch_on_current_device(const char* fn, void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(OSCAR_EHIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(OSCAR_EHIP, "%s: device %d beyond the %d supported", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(OSCAR_EHIP, "%s: hipGetSymbolAddress of the scratch array failed on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return OSCAR_OK;
+}
+
 }  // namespace
 }  // namespace oscar
 
@@ -305,6 +337,32 @@ oscar_status oscar_decode_attn_append(const oscar_kv_cache* cache, const int32_t
   int32_t splits = 0;
   oscar_status st = decode_int2_splits(fn, cache, n_quant, n_tail, max_tokens, q, num_q_heads, sm_scale, k_new,
                                        v_new, out, true, ws, ws_bytes, s, &splits);
+  if (st != OSCAR_OK) return st;
+  return launched(launch_merge(static_cast<const float*>(ws), out, cache->batch, num_q_heads, splits, s), fn);
+}
+
+oscar_status oscar_decode_attn_noalloc(const oscar_kv_cache* cache, const int32_t* n_quant, const int32_t* n_tail,
+                                       int32_t max_tokens, const uint16_t* q, int32_t num_q_heads, float sm_scale,
+                                       float* out, void* stream) {
+  const char* fn = "oscar_decode_attn_noalloc";
+  // the size check comes first, so that a shape beyond the array is refused
+  // before anything touches the device
+  const size_t need = (cache != nullptr && num_q_heads > 0)
+                          ? oscar_decode_workspace_bytes(cache->batch, cache->num_kv_heads, num_q_heads, max_tokens)
+                          : 0;
+  if (need > OSCAR_NOALLOC_SCRATCH_BYTES)
+    return fail(OSCAR_EWORKSPACE, "%s: this shape needs %zu bytes of split records, more than the %d-byte scratch array",
+                fn, need, OSCAR_NOALLOC_SCRATCH_BYTES);
+  oscar_status st = check_cache(fn, cache);
+  if (st != OSCAR_OK) return st;
+  if ((st = check_heads(fn, cache->batch, cache->num_kv_heads, num_q_heads)) != OSCAR_OK) return st;
+  if ((st = check_device(fn)) != OSCAR_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_on_current_device(fn, &ws)) != OSCAR_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t splits = 0;
+  st = decode_int2_splits(fn, cache, n_quant, n_tail, max_tokens, q, num_q_heads, sm_scale, nullptr, nullptr, out,
+                          true, ws, OSCAR_NOALLOC_SCRATCH_BYTES, s, &splits);
   if (st != OSCAR_OK) return st;
   return launched(launch_merge(static_cast<const float*>(ws), out, cache->batch, num_q_heads, splits, s), fn);
 }

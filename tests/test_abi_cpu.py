@@ -204,3 +204,29 @@ def test_bf16_validation_errors():
     assert d(mt=2048) == ob.OSCAR_EINVAL
     assert d(ws_bytes=10) == ob.OSCAR_EWORKSPACE
     assert d() == ob.OSCAR_EHIP
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch_array():
+    """oscar_decode_attn_noalloc checks the record size against its fixed
+    array before anything else, GPU or not: 1024 sequences of 64 query heads
+    need 1024 * 64 * 528 bytes, more than 4 MiB."""
+    L = ob.lib()
+    need = ob.decode_workspace_bytes(1024, 8, 64, 1024)
+    assert need > ob.NOALLOC_SCRATCH_BYTES
+    st = L.oscar_decode_attn_noalloc(ctypes.byref(_desc(batch=1024)), 0x100, 0x200, 1024, 0x80000, 64, 0.088,
+                                     0x90000, None)
+    assert st == 3
+    assert b"scratch" in L.oscar_last_error()
+    # the 128K layer (32 splits of 32 query heads) and batch 8 fit
+    assert ob.decode_workspace_bytes(1, 8, 32, 131072) <= ob.NOALLOC_SCRATCH_BYTES
+    assert ob.decode_workspace_bytes(8, 8, 32, 131072) <= ob.NOALLOC_SCRATCH_BYTES
+
+
+@needs_no_gpu
+def test_noalloc_validation_without_a_device():
+    L = ob.lib()
+    st = L.oscar_decode_attn_noalloc(ctypes.byref(_desc(head_dim=64)), 0x100, 0x200, 1024, 0x80000, 32, 0.088,
+                                     0x90000, None)
+    assert st == 2
+    st = L.oscar_decode_attn_noalloc(ctypes.byref(_desc()), 0x100, 0x200, 1024, 0x80000, 32, 0.088, 0x90000, None)
+    assert st == 4 and b"no HIP device" in L.oscar_last_error()

@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--bf16-copies", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target seconds of oracle work")
-    p.add_argument("--profile", choices=["none", "int2", "bf16", "quantize", "copy"], default="none",
+    p.add_argument("--profile", choices=["none", "int2", "bf16", "quantize", "copy", "stream"], default="none",
                    help="run only one kernel (for rocprofv3 runs) and print its timing")
     p.add_argument("--ablation", action="store_true",
                    help="Token Norm Imbalance ablation on the 128K layer: attention-output error of each "
@@ -90,9 +90,22 @@ def traffic_record(launch_bytes):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(target_s):
     """The oracle (numpy float64, unmodified) on one KV-head slice of the
-    128K workload: quantize once (untimed), then repeated decode steps."""
+    128K workload: the prefill quantize of the slice (median of 3), then
+    repeated decode steps for about target_s seconds."""
+    import statistics
     import numpy as np
     import oracle
     import synthetic as syn
@@ -101,10 +114,16 @@ def cpu_baseline(target_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    host_cores = len(os.sched_getaffinity(0))
     w = syn.workload(3)
     k = syn.bf16_bits_to_f64(syn.keys_slice(w, 0, 0))
     v = syn.bf16_bits_to_f64(syn.values_slice(w, 0, 0))
-    s = oracle.quantize_slice(k, v, 131072)
+    qt = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        s = oracle.quantize_slice(k, v, 131072)
+        qt.append(time.perf_counter() - t0)
+    quant_s = statistics.median(qt)
     del k, v
     q = syn.bf16_bits_to_f64(syn.query(w, 0)[:4])
     sm = 1.0 / np.sqrt(128.0)
@@ -116,10 +135,17 @@ def cpu_baseline(target_s):
         if el >= target_s:
             break
     bytes_per_rep = 131072 * BYTES_PER_TOKEN_HEAD + 4 * 128 * 2 + 4 * 128 * 4
-    return {"value": round(bytes_per_rep * reps / el / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+    quant_bytes = 131072 * (BF16_BYTES_PER_TOKEN_HEAD + BYTES_PER_TOKEN_HEAD)
+    return {"value": round(bytes_per_rep * reps / el / 1e9, 4), "unit": "GB/s", "cores": int(min(threads, host_cores)),
             "kind": "oracle",
             "sample": f"oracle decode of 1 of 8 KV heads (4 query heads) over 131072 quantized tokens, "
-                      f"{reps} repetitions in {el:.1f} s; GB/s = algorithmic bytes of those steps / time"}
+                      f"{reps} repetitions in {el:.1f} s; GB/s = algorithmic bytes of those steps / time",
+            "decode_ms_per_slice": round(1e3 * el / reps, 2),
+            "quantize_prefill_ms_per_slice_median_of_3": round(1e3 * quant_s, 1),
+            "quantize_prefill_GBs": round(quant_bytes / quant_s / 1e9, 4),
+            "quantize_sample": "oracle prefill quantize (rotate, norm, scale, key/value params and codes, pack) "
+                               "of 1 of 8 KV heads, 131072 tokens",
+            "blas_threads": int(threads), "host_cores": host_cores, "cpu_model": cpu_model()}
 
 
 def graph_step_us(calls, replays):
@@ -142,6 +168,54 @@ def graph_step_us(calls, replays):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / (replays * len(calls))
+
+
+def stream_probe_us(caches, B, H, T, splits, n, stream):
+    """Time per launch (us) of the decode kernel's cache stream without
+    compute, over the same cache copies, back to back (median of 5 regions)."""
+    import ctypes
+    import torch
+    from kv_cache_int2_fwht_amd import probes
+    L = probes.lib()
+    sink = torch.empty(B * H * splits * 2, dtype=torch.int32, device=caches[0].blocks.device)
+
+    def launch(i):
+        st = L.oscar_probe_stream(caches[i % len(caches)].blocks.data_ptr(), B, H, T, splits, sink.data_ptr(),
+                                  ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"oscar_probe_stream failed ({st})")
+
+    for i in range(max(4, n // 10)):
+        launch(i)
+    runs = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            launch(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        runs.append(e0.elapsed_time(e1) * 1e3 / n)
+    return sorted(runs)[2]
+
+
+def shader_clock_mhz(stream):
+    """Shader clock measured by the clock probe (256 one-wave workgroups),
+    launched on `stream` right behind whatever it holds: the clock the chip
+    runs at once the preceding work ends.  Median over the workgroups."""
+    import ctypes
+    import statistics
+    import torch
+    from kv_cache_int2_fwht_amd import probes
+    L = probes.lib()
+    khz = L.oscar_probe_wall_clock_khz()
+    out = torch.zeros(256 * 3, dtype=torch.int64, device="cuda")
+    if L.oscar_probe_clock(out.data_ptr(), 256, 20000, ctypes.c_void_p(stream.cuda_stream)) != 0 or khz <= 0:
+        return None
+    torch.cuda.synchronize()
+    o = out.view(256, 3).cpu().tolist()
+    return round(statistics.median(c / r * khz / 1e3 for c, r, _ in o if r > 0), 1)
 
 
 def context_sweep(args):
@@ -700,13 +774,24 @@ def main():
         ob.decode_attn(caches[i % len(caches)], nq, nt, T, q, sm, out, ws, stream=stream)
 
     int2_bytes = B * H * T * BYTES_PER_TOKEN_HEAD + B * Hq * 128 * (2 + 4)
+    splits = ob.decode_num_splits(B, H, T)
+    if args.profile == "stream":
+        print(json.dumps({"profile": "stream", "us_per_launch": stream_probe_us(caches, B, H, T, splits,
+                                                                                 args.steps, stream)}))
+        return
     for i in range(args.warmup):
         int2_step(i)
     torch.cuda.synchronize()
     int2_us = timed(int2_step, args.steps)
+    # the shader clock right behind the timed steps (before the chip idles)
+    for i in range(args.warmup):
+        int2_step(i)
+    sclk = shader_clock_mhz(stream)
     if args.profile == "int2":
         print(json.dumps({"profile": "int2", "us_per_step": int2_us}))
         return
+    # the distribution of single steps, each bracketed by its own events
+    step_p10, step_p50, step_p90 = timed_each(int2_step, args.steps)
 
     # ---- the dominant kernel alone: the INT2 decode kernel (split records) ----
     def int2_kernel(i):
@@ -722,6 +807,8 @@ def main():
     kern_runs = sorted(timed(int2_kernel, args.steps) for _ in range(5))
     kern_us = kern_runs[2]
     kern_p10, kern_med_us, kern_p90 = timed_each(int2_kernel, args.steps)
+    # the attainable bound: the same stream without compute
+    probe_us = stream_probe_us(caches, B, H, T, splits, args.steps, stream)
     # the same steps replayed from a HIP graph (no per-call host cost)
     int2_graph_us = graph_step_us([lambda c=c: ob.decode_attn(c, nq, nt, T, q, sm, out, ws) for c in caches],
                                   max(2, args.steps // len(caches)))
@@ -762,15 +849,24 @@ def main():
         "config": {"workload": "llama31-8b-layer-128k", "batch": B, "q_heads": Hq, "kv_heads": H,
                    "head_dim": 128, "context": T, "tail": 0, "cache_copies": len(caches)},
         "us_per_step": round(int2_us, 3),
+        "us_per_step_single_p10_p50_p90": [round(step_p10, 3), round(step_p50, 3), round(step_p90, 3)],
         "us_per_step_graph_replay": round(int2_graph_us, 3),
         "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(B / (int2_us * 1e-6), 1),
         "roofline": {"bound": "hbm", "achieved": round(kern_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kern_achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_int2_kernel<4>", "algorithmic_bytes_per_launch": int2_bytes,
-                     "kernel_us_mean": round(kern_us, 3),
-                     "kernel_us_mean_of_5_regions": [round(x, 3) for x in kern_runs],
-                     "kernel_us_isolated_p10_p50_p90": [round(kern_p10, 3), round(kern_med_us, 3), round(kern_p90, 3)]},
+                     "kernel_us_per_launch": round(kern_us, 3),
+                     "kernel_us_per_launch_note": "median over 5 timed regions of the mean launch duration of "
+                                                  f"{args.steps} back-to-back launches (events on the launch stream)",
+                     "kernel_us_per_launch_5_regions": [round(x, 3) for x in kern_runs],
+                     "kernel_us_isolated_p10_p50_p90": [round(kern_p10, 3), round(kern_med_us, 3), round(kern_p90, 3)],
+                     "attainable": {"probe": "the same cache stream without compute (oscar_probe_stream)",
+                                    "us_per_launch": round(probe_us, 3),
+                                    "GBs": round(int2_bytes / (probe_us * 1e-6) / 1e9, 2),
+                                    "frac_of_peak": round(int2_bytes / (probe_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+                     "pct_of_attainable": round(100 * probe_us / kern_us, 2)},
+        "sclk_mhz_after_steps": sclk,
         "bf16_reference": {"us_per_step": round(bf16_us, 3),
                            "achieved_GBs": round(bf16_bytes / (bf16_us * 1e-6) / 1e9, 2),
                            "algorithmic_bytes_per_launch": bf16_bytes},

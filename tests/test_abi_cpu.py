@@ -34,6 +34,21 @@ def test_library_exports_every_declared_function():
     assert set(declared) == set(ob.EXPORTED)
 
 
+def test_probe_library_exports_every_declared_function():
+    from kv_cache_int2_fwht_amd import probes
+    text = open(os.path.join(ROOT, "include", "oscar_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    declared = sorted(set(re.findall(r"\b(oscar_[a-z0-9_]+)\s*\(", text)))
+    assert set(declared) == set(probes.EXPORTED)
+    L = probes.lib()
+    for name in declared:
+        assert hasattr(L, name), f"{name} declared in oscar_probe.h but not exported"
+    # invalid arguments are refused before any launch
+    assert L.oscar_probe_stream(0, 1, 8, 1024, 32, 0x1000, None) == 1
+    assert L.oscar_probe_stream(0x10000, 1, 8, 1000, 32, 0x1000, None) == 1
+    assert L.oscar_probe_clock(0, 256, 100, None) == 1
+
+
 def test_version_and_status_strings():
     assert ob.abi_version() == 3
     assert ob.status_string(0) == "ok"

@@ -126,21 +126,33 @@ __device__ __forceinline__ float digits_value(const v4i& c) {
   return fmaf(static_cast<float>(hi), 65536.f, static_cast<float>(lo));
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 struct GroupBytes {
-  uint2 kd[8];     // K codes of token tau(4c+b) (see lane roles), dwords 2g and 2g+1 of the row
-  uint2 vd[8];     // V codes of channel 16j + n, dwords 2g and 2g+1 of the channel row
+  u32x2 kd[8];      // K codes of token tau(4c+b) (see lane roles), dwords 2g and 2g+1 of the row
+  u32x2 vd[8];      // V codes of channel 16j + n, dwords 2g and 2g+1 of the channel row
   uint32_t nrm[4];  // fp16 norms of tokens 16w + 4b + u + {0, 1}
-  uint2 vsz[4];     // (vs | vz << 16) of tokens 16w + 4b + u + {0, 1}
-  uint2 ksz[4];     // (s | z << 16) of channels 16w + 4b + u + {0, 1}
+  u32x2 vsz[4];     // (vs | vz << 16) of tokens 16w + 4b + u + {0, 1}
+  u32x2 ksz[4];     // (s | z << 16) of channels 16w + 4b + u + {0, 1}
 };
 
 // A group's block in LDS, as a loader wave copies it with direct global ->
 // LDS loads (16 bytes per lane per instruction, one contiguous kilobyte per
-// wave instruction): the block's own layout, except that the key code rows
-// are permuted (k_slot).  Compute waves read their lane's operands from it
-// (read_stage).
-constexpr int kStageK = OSCAR_BLOCK_K_CODES;   // 4096 B: key code half rows (16 B), order given by k_slot
-constexpr int kStageV = OSCAR_BLOCK_V_CODES;   // 4096 B: value code rows, channel-major
+// wave instruction).  The copies permute the block's 16-byte pieces so that
+// the compute waves' 8-byte operand reads are free of LDS bank conflicts
+// (gfx950 serves 32 lanes of an 8-byte read per cycle from 64 four-byte
+// banks, so each read instruction should cover 256 contiguous bytes per 32
+// lanes):
+//  * key codes: slot 16 (4 b + 2 c + hh) + n holds half hh (16 bytes) of the
+//    row of token 16 (n >> 1) + 4 b + 2 (n & 1) + c, the token of column n of
+//    score tile 4 c + b (see the lane roles above);
+//  * value codes: slot 32 j + 16 hh + n holds half hh of the row of channel
+//    16 j + n;
+//  * key and value (s, z) pairs: 16-byte piece p (four channels or tokens) of
+//    each 512-byte array at slot p ^ 2 ((p >> 4) & 1);
+//  * norms: 16-byte piece p (eight tokens) at slot p ^ ((p >> 3) & 1) (a
+//    4-byte read serves 32 lanes per cycle from 32 banks).
+constexpr int kStageK = OSCAR_BLOCK_K_CODES;   // 4096 B: key code half rows
+constexpr int kStageV = OSCAR_BLOCK_V_CODES;   // 4096 B: value code half rows
 constexpr int kStageKsz = OSCAR_BLOCK_K_SZ;    // 512 B: (s, z) per channel
 constexpr int kStageVsz = OSCAR_BLOCK_V_SZ;    // 512 B: (vs, vz) per token
 constexpr int kStageNorm = OSCAR_BLOCK_K_NORM; // 256 B: fp16 norms
@@ -150,9 +162,8 @@ static_assert(kStageV == 4096 && kStageKsz == 8192 && kStageVsz == kStageKsz + 5
                   kStageBytes == 9472,
               "the copy below assumes this block layout");
 
-// LDS slot of half row hh of token t: the XOR with bit 4 of t makes the
-// 8-byte reads of a score tile hit every bank equally often.
-__device__ __forceinline__ int k_slot(int t, int hh) { return 2 * (t ^ ((t >> 4) & 1)) + hh; }
+__device__ __forceinline__ int sz_piece_slot(int p) { return p ^ (((p >> 4) & 1) << 1); }   // an involution
+__device__ __forceinline__ int norm_piece_slot(int p) { return p ^ ((p >> 3) & 1); }        // an involution
 
 // One 16-byte-per-lane global -> LDS load: lane l's 16 bytes at gptr land at
 // LDS byte lds + 16 l (lanes switched off write nothing).  Issued as inline
@@ -166,18 +177,46 @@ __device__ __forceinline__ void lds_load16(const void* gptr, const uint8_t* lds)
                : "memory");
 }
 
-// The kDmaPerGroup loads that copy the group block at blk into a stage.
-__device__ __forceinline__ void dma_group(uint8_t* stage, const uint8_t* blk, int lane) {
+// Source byte offsets, inside a group block, of the 16 bytes a loader lane
+// copies with each of the group's load instructions (fixed for the kernel).
+struct LoaderLane {
+  int k[4];   // key code slots 64 j + lane
+  int v[4];   // value code slots 64 j + lane
+  int sz;     // (s, z) slot lane of the 1 KB of pairs
+  int nrm;    // norm slot lane (lanes 0..15)
+};
+
+__device__ __forceinline__ LoaderLane loader_lane(int lane) {
+  LoaderLane o;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int sl = 64 * j + lane;                       // stage slot this lane fills
-    const int t = (sl >> 1) ^ ((sl >> 5) & 1);          // the inverse of k_slot
-    lds_load16(blk + kStageK + t * 32 + 16 * (sl & 1), stage + kStageK + 1024 * j);
+    const int sl = 64 * j + lane;
+    const int cls = sl >> 4, n = sl & 15;
+    const int b = cls >> 2, c = (cls >> 1) & 1, hh = cls & 1;
+    o.k[j] = kStageK + 32 * (16 * (n >> 1) + 4 * b + 2 * (n & 1) + c) + 16 * hh;
+    o.v[j] = kStageV + 32 * (16 * (sl >> 5) + n) + 16 * ((sl >> 4) & 1);
   }
-  // value codes, then the key and value (s, z) pairs: 5 contiguous kilobytes
+  o.sz = kStageKsz + 512 * (lane >> 5) + 16 * sz_piece_slot(lane & 31);
+  o.nrm = kStageNorm + 16 * norm_piece_slot(lane & 15);
+  return o;
+}
+
+// The kDmaPerGroup loads that copy the group block at blk into a stage.
+__device__ __forceinline__ void dma_group(uint8_t* stage, const uint8_t* blk, const LoaderLane& o, int lane) {
 #pragma unroll
-  for (int j = 0; j < 5; ++j) lds_load16(blk + kStageV + 1024 * j + 16 * lane, stage + kStageV + 1024 * j);
-  if (lane < 16) lds_load16(blk + kStageNorm + 16 * lane, stage + kStageNorm);
+  for (int j = 0; j < 4; ++j) lds_load16(blk + o.k[j], stage + kStageK + 1024 * j);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) lds_load16(blk + o.v[j], stage + kStageV + 1024 * j);
+  lds_load16(blk + o.sz, stage + kStageKsz);
+  if (lane < 16) lds_load16(blk + o.nrm, stage + kStageNorm);
+}
+
+// An LDS flag, read by lane 0 alone and broadcast to the wave (a read of
+// one word by all 64 lanes occupies the LDS longer).
+__device__ __forceinline__ int read_flag(const int* f, int lane) {
+  int v = 0;
+  if (lane == 0) v = __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return __builtin_amdgcn_readfirstlane(v);
 }
 
 // Wait until at most `rem` groups' copies of this wave are outstanding
@@ -196,48 +235,91 @@ __device__ __forceinline__ void wait_groups_outstanding(int rem) {
 }
 
 // Byte offsets inside a stage of the operands a lane reads (see the lane
-// roles above), fixed for the whole kernel, so that each read of a group is
-// one of these plus an immediate.  Key rows: token t = base + 4 b + c of
-// tile 4 c + b sits at half-row slot k_slot(t, gl / 2); since t / 16 = w and
-// bit 0 of t is c, that is byte 32 (base + 4 b + (c ^ (w & 1))) + 8 gl.
+// roles above and the stage layout), fixed for the whole kernel, so that
+// each read of a group is one of these plus an immediate.
 struct StageLane {
-  int k[2];   // key codes of the tiles with c = 0, 1 (+ 128 b)
-  int v;      // value codes of channel n (+ 512 j)
-  int nrm;    // norms of tokens base + 4 b (+ 8 b)
-  int vsz;    // value (s, z) of tokens base + 4 b (+ 16 b)
-  int ksz;    // key (s, z) of channels base + 4 b (+ 16 b)
+  int k;      // key codes of tile 4 c + b: + 512 c + 1024 b
+  int v;      // value codes of channel tile j: + 512 j
+  int nrm[2]; // norms of tokens base + 4 b: nrm[b >> 1] + 8 (b & 1)
+  int vsz[2]; // value (s, z) of tokens base + 4 b: vsz[b >> 1] + 16 b
+  int ksz[2]; // key (s, z) of channels base + 4 b: ksz[b >> 1] + 16 b
 };
 
 __device__ __forceinline__ StageLane stage_lane(int lane) {
   const int gl = lane >> 4;
   const int n = lane & 15;
-  const int w1 = (n >> 1) & 1;
-  const int base = 16 * (n >> 1) + 2 * (n & 1);   // token / channel 16w + u
+  const int w = n >> 1;
   StageLane o;
-  o.k[0] = kStageK + 32 * (base + w1) + 8 * gl;
-  o.k[1] = kStageK + 32 * (base + 1 - w1) + 8 * gl;
-  o.v = kStageV + 32 * n + 8 * gl;
-  o.nrm = kStageNorm + 2 * base;
-  o.vsz = kStageVsz + 4 * base;
-  o.ksz = kStageKsz + 4 * base;
+  const int half = 256 * (gl >> 1) + 16 * n + 8 * (gl & 1);
+  o.k = kStageK + half;
+  o.v = kStageV + half;
+  // norms of tokens 16 w + 4 b + u (+1): piece 2 w + (b >> 1) at slot
+  // (2 w + (b >> 1)) ^ s, s = w >> 2, at byte 8 (b & 1) + 2 u of the piece
+  const int sn = w >> 2;
+  o.nrm[0] = kStageNorm + 32 * w + 16 * sn + 4 * (n & 1);
+  o.nrm[1] = kStageNorm + 32 * w + 16 * (1 - sn) + 4 * (n & 1);
+  // (s, z) of channels / tokens 16 w + 4 b + u (+1): piece 4 w + b at slot
+  // (4 w + b) ^ x, x = 2 (w >> 2): 4 w + b + x for b < 2, 4 w + b - x for b >= 2
+  const int x = 2 * (w >> 2);
+  const int pair = 64 * w + 8 * (n & 1);
+  o.vsz[0] = kStageVsz + pair + 16 * x;
+  o.vsz[1] = kStageVsz + pair - 16 * x;
+  o.ksz[0] = kStageKsz + pair + 16 * x;
+  o.ksz[1] = kStageKsz + pair - 16 * x;
   return o;
 }
 
-// Registers of the group being computed.
+// Registers of the group being computed: 28 single LDS reads in one block,
+// which waits for all of them at its end.  (Left to itself the compiler
+// pairs reads 512 or 16 bytes apart into one paired instruction, which
+// gfx950 serves with bank conflicts for these layouts; single reads of the
+// layouts above have none.)
 __device__ __forceinline__ void read_stage(GroupBytes& r, const uint8_t* stage, const StageLane& o) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r.kd[i] = *reinterpret_cast<const uint2*>(stage + o.k[i >> 2] + 128 * (i & 3));
-#pragma unroll
-  for (int j = 0; j < 8; ++j) r.vd[j] = *reinterpret_cast<const uint2*>(stage + o.v + 512 * j);
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    r.nrm[b] = *reinterpret_cast<const uint32_t*>(stage + o.nrm + 8 * b);
-    r.vsz[b] = *reinterpret_cast<const uint2*>(stage + o.vsz + 16 * b);
-    r.ksz[b] = *reinterpret_cast<const uint2*>(stage + o.ksz + 16 * b);
-  }
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage));
+  const uint32_t ak = base + o.k, av = base + o.v;
+  const uint32_t an0 = base + o.nrm[0], an1 = base + o.nrm[1];
+  const uint32_t avs0 = base + o.vsz[0], avs1 = base + o.vsz[1];
+  const uint32_t aks0 = base + o.ksz[0], aks1 = base + o.ksz[1];
+  asm volatile(
+      "ds_read_b64 %0, %28\n\t"
+      "ds_read_b64 %1, %28 offset:1024\n\t"
+      "ds_read_b64 %2, %28 offset:2048\n\t"
+      "ds_read_b64 %3, %28 offset:3072\n\t"
+      "ds_read_b64 %4, %28 offset:512\n\t"
+      "ds_read_b64 %5, %28 offset:1536\n\t"
+      "ds_read_b64 %6, %28 offset:2560\n\t"
+      "ds_read_b64 %7, %28 offset:3584\n\t"
+      "ds_read_b64 %8, %29\n\t"
+      "ds_read_b64 %9, %29 offset:512\n\t"
+      "ds_read_b64 %10, %29 offset:1024\n\t"
+      "ds_read_b64 %11, %29 offset:1536\n\t"
+      "ds_read_b64 %12, %29 offset:2048\n\t"
+      "ds_read_b64 %13, %29 offset:2560\n\t"
+      "ds_read_b64 %14, %29 offset:3072\n\t"
+      "ds_read_b64 %15, %29 offset:3584\n\t"
+      "ds_read_b32 %16, %30\n\t"
+      "ds_read_b32 %17, %30 offset:8\n\t"
+      "ds_read_b32 %18, %31\n\t"
+      "ds_read_b32 %19, %31 offset:8\n\t"
+      "ds_read_b64 %20, %32\n\t"
+      "ds_read_b64 %21, %32 offset:16\n\t"
+      "ds_read_b64 %22, %33 offset:32\n\t"
+      "ds_read_b64 %23, %33 offset:48\n\t"
+      "ds_read_b64 %24, %34\n\t"
+      "ds_read_b64 %25, %34 offset:16\n\t"
+      "ds_read_b64 %26, %35 offset:32\n\t"
+      "ds_read_b64 %27, %35 offset:48\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r.kd[0]), "=&v"(r.kd[1]), "=&v"(r.kd[2]), "=&v"(r.kd[3]), "=&v"(r.kd[4]), "=&v"(r.kd[5]),
+        "=&v"(r.kd[6]), "=&v"(r.kd[7]), "=&v"(r.vd[0]), "=&v"(r.vd[1]), "=&v"(r.vd[2]), "=&v"(r.vd[3]),
+        "=&v"(r.vd[4]), "=&v"(r.vd[5]), "=&v"(r.vd[6]), "=&v"(r.vd[7]), "=&v"(r.nrm[0]), "=&v"(r.nrm[1]),
+        "=&v"(r.nrm[2]), "=&v"(r.nrm[3]), "=&v"(r.vsz[0]), "=&v"(r.vsz[1]), "=&v"(r.vsz[2]), "=&v"(r.vsz[3]),
+        "=&v"(r.ksz[0]), "=&v"(r.ksz[1]), "=&v"(r.ksz[2]), "=&v"(r.ksz[3])
+      : "v"(ak), "v"(av), "v"(an0), "v"(an1), "v"(avs0), "v"(avs1), "v"(aks0), "v"(aks1)
+      : "memory");
 }
 
-__device__ __forceinline__ uint32_t pick(const uint2& v, int c) { return c ? v.y : v.x; }
+__device__ __forceinline__ uint32_t pick(const u32x2& v, int c) { return c ? v.y : v.x; }
 __device__ __forceinline__ float f16_lo(uint32_t w) { return f16_bits_to_f32(static_cast<uint16_t>(w & 0xffffu)); }
 __device__ __forceinline__ float f16_hi(uint32_t w) { return f16_bits_to_f32(static_cast<uint16_t>(w >> 16)); }
 
@@ -570,12 +652,13 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
   };
   int issued = 0;   // groups this loader has requested, in order (its j-th is k = wave + j kLoaders)
   if (loader) {
+    const LoaderLane ll = loader_lane(lane);
     static_assert(C::kAhead * C::kLoaders <= C::kRing, "the first groups go to unused stages");
 #pragma unroll
     for (int j = 0; j < C::kAhead; ++j) {
       const int k = wave + j * C::kLoaders;
       if (split + k * S >= groups_cap) break;
-      dma_group(sm.ring[k % C::kRing], group_block(k), lane);
+      dma_group(sm.ring[k % C::kRing], group_block(k), ll, lane);
       ++issued;
     }
   }
@@ -615,6 +698,7 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
     // wave's in-order vector-memory counter shows when only the loads of
     // later groups are outstanding.
     const int n_mine = (n_k > wave) ? (n_k - wave + C::kLoaders - 1) / C::kLoaders : 0;
+    const LoaderLane ll = loader_lane(lane);
     // the block of the next group to request, looked up one request ahead
     // (a paged cache's table entry is then read long before it is needed)
     const uint8_t* next_blk = (issued < n_mine) ? group_block(wave + issued * C::kLoaders) : a.blocks;
@@ -625,15 +709,18 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
         const int use = k / C::kRing;   // earlier occupants of the stage
         const uint8_t* blk = next_blk;
         if (issued + 1 < n_mine) next_blk = group_block(k + C::kLoaders);
-        while (__hip_atomic_load(&sm.emptied[s], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < use)
+        while (read_flag(&sm.emptied[s], lane) < use)
           __builtin_amdgcn_s_sleep(1);
-        dma_group(sm.ring[s], blk, lane);
+        dma_group(sm.ring[s], blk, ll, lane);
       }
       // the counter wait is the release: the copies are in LDS before the
       // flag store issues (a release store would wait for every load)
       wait_groups_outstanding<C::kAhead - 1>(issued - 1 - j);
       const int k = wave + j * C::kLoaders;
-      __hip_atomic_store(&sm.filled[k % C::kRing], k / C::kRing + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      // one lane stores the flag (a store of all 64 lanes to one word would
+      // occupy the LDS for many cycles)
+      if (lane == 0)
+        __hip_atomic_store(&sm.filled[k % C::kRing], k / C::kRing + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // first groups requested for nothing included
   } else {
@@ -679,7 +766,7 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
       // every lane releases its own writes
       __hip_atomic_store(&sm.q_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    while (__hip_atomic_load(&sm.q_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+    while (read_flag(&sm.q_ready, lane) == 0)
       __builtin_amdgcn_s_sleep(1);
     // query of this lane's head and channels 16w + 4b + u + c, per row block:
     // rotated like the keys (unrotated only for the ablation variant whose
@@ -710,12 +797,12 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
     for (int k = simd + 4 * (wave / 4 - first_i); k < n_k; k += 4 * n_simd) {
       const int s = k % C::kRing;
       const int use = k / C::kRing;
-      while (__hip_atomic_load(&sm.filled[s], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <= use)
+      while (read_flag(&sm.filled[s], lane) <= use)
         __builtin_amdgcn_s_sleep(1);
       read_stage(cur, sm.ring[s], sl);
       // the stage may be refilled once every lane's reads have returned
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __hip_atomic_store(&sm.emptied[s], use + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (lane == 0) __hip_atomic_store(&sm.emptied[s], use + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       // The last group of each SIMD (one of the split's last four) lands when
       // the stream ends and bounds the kernel's end, while the other waves
       // on its SIMD finish groups that landed earlier: it is issued first.

@@ -446,6 +446,10 @@ struct Int2Smem {
   // values' p digits)
   uint8_t a_op[Int2Cfg<G>::kCompute][Int2Cfg<G>::kRB][2 * 4 * kOpBlock];
   uint8_t ring[Int2Cfg<G>::kRing][kStageBytes];      // group stages
+  // key (s, z) pairs of the split's last four groups, group k at [k % 4],
+  // in the stage's piece order, fetched at the start by the waves that
+  // compute them
+  uint8_t last_ksz[4][512];
   MergeSmem<G, Int2Cfg<G>::kSlots> merge;              // final state of each compute wave, and of the bf16 tail
   int filled[Int2Cfg<G>::kRing];    // stage s holds group index k = s + kRing * (filled[s] - 1)
   int emptied[Int2Cfg<G>::kRing];   // times stage s has been read into registers
@@ -460,18 +464,20 @@ struct WaveRun {
   float m[RB], l[RB], z[RB], acc[RB][8];
 };
 
-// Score phase of one quantized 128-token group: scores on the matrix cores,
-// online softmax update, p * vs staged as the value phase's A operand.
-// Returns the softmax rescale factors in alpha and inv_p.
-template <int G>
-__device__ __forceinline__ void score_phase(const GroupBytes& cur, int t0, int t_end,
-                                            const float (&qv)[Int2Cfg<G>::kRB][2][4], const float (&fac)[2],
-                                            Int2Smem<G>& sm, WaveRun<Int2Cfg<G>::kRB>& st, int wave, int gl, int n,
-                                            float (&alpha)[Int2Cfg<G>::kRB], float (&inv_p)[Int2Cfg<G>::kRB]) {
-  constexpr int RB = Int2Cfg<G>::kRB;
-  const int tok_base = t0 + 16 * (n >> 1) + 2 * (n & 1);
-  // ---- q' = Hq * s16 as 4-digit fixed point (A operand), Z = Hq . z16 ----
+// The query side of a group's scores, which depends only on the group's key
+// (s, z) pairs: the A operand q' = Hq * s16 as 4-digit fixed point (staged
+// and read back), its top-field bias, Z = Hq . z16 and the scale back.
+template <int RB>
+struct QPrep {
+  v4i aq[RB][2], bias[RB];
   float Zg[RB], inv_q[RB];
+};
+
+template <int G>
+__device__ __forceinline__ void q_prep(const u32x2 (&ksz)[4], const float (&qv)[Int2Cfg<G>::kRB][2][4],
+                                       const float (&fac)[2], Int2Smem<G>& sm, int wave, int gl, int n,
+                                       QPrep<Int2Cfg<G>::kRB>& p) {
+  constexpr int RB = Int2Cfg<G>::kRB;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     float qs[2][4];
@@ -480,17 +486,17 @@ __device__ __forceinline__ void score_phase(const GroupBytes& cur, int t0, int t
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const uint32_t w = pick(cur.ksz[b], c);
+        const uint32_t w = pick(ksz[b], c);
         qs[c][b] = fmaf(qv[rb][c][b], f16_lo(w), 0.f);   // one mixed-precision FMA
         zp = fmaf(qv[rb][c][b], f16_hi(w), zp);
         amax = fmaxf(amax, fabsf(qs[c][b]));
       }
     amax = row_max16_nonneg(amax);
-    Zg[rb] = row_sum16(zp);
+    p.Zg[rb] = row_sum16(zp);
     int e;
     frexpf(amax, &e);                        // amax < 2^e
     const float sc = ldexpf(1.f, 24 - e);    // |q' * sc| < 2^24, |q' * sc * fac| < 2^30
-    inv_q[rb] = ldexpf(1.f, e - 30);         // 1 / (sc * 64)
+    p.inv_q[rb] = ldexpf(1.f, e - 30);       // 1 / (sc * 64)
     uint32_t x[2][4];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -499,13 +505,25 @@ __device__ __forceinline__ void score_phase(const GroupBytes& cur, int t0, int t
     stage_digits(sm.a_op[wave][rb], x, gl, n);
   }
   wave_sync_lds();
-  v4i aq[RB][2], bias[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    aq[rb][0] = read_operand(sm.a_op[wave][rb], 0, gl, n);
-    aq[rb][1] = read_operand(sm.a_op[wave][rb], 1, gl, n);
-    bias[rb] = field3_bias(aq[rb][0], aq[rb][1]);
+    p.aq[rb][0] = read_operand(sm.a_op[wave][rb], 0, gl, n);
+    p.aq[rb][1] = read_operand(sm.a_op[wave][rb], 1, gl, n);
+    p.bias[rb] = field3_bias(p.aq[rb][0], p.aq[rb][1]);
   }
+}
+
+// Score phase of one quantized 128-token group with its query side p:
+// scores on the matrix cores, online softmax update, p * vs staged as the
+// value phase's A operand.  Returns the softmax rescale factors in alpha
+// and inv_p.
+template <int G>
+__device__ __forceinline__ void score_phase(const GroupBytes& cur, const QPrep<Int2Cfg<G>::kRB>& p, int t0, int t_end,
+                                            Int2Smem<G>& sm, WaveRun<Int2Cfg<G>::kRB>& st, int wave, int gl, int n,
+                                            const float (&fac)[2], float (&alpha)[Int2Cfg<G>::kRB],
+                                            float (&inv_p)[Int2Cfg<G>::kRB]) {
+  constexpr int RB = Int2Cfg<G>::kRB;
+  const int tok_base = t0 + 16 * (n >> 1) + 2 * (n & 1);
 
   // ---- scores: column n of tile i = 4c + b is token 16w + 4b + u + c ----
   float logit[RB][2][4];
@@ -517,9 +535,9 @@ __device__ __forceinline__ void score_phase(const GroupBytes& cur, int t0, int t
     const float n16 = c ? f16_hi(cur.nrm[b]) : f16_lo(cur.nrm[b]);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[rb][0], b0, bias[rb], 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[rb][1], b1, acc, 0, 0, 0);
-      logit[rb][c][b] = fmaf(fmaf(digits_value(acc), inv_q[rb], Zg[rb]), n16, 0.f);
+      v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(p.aq[rb][0], b0, p.bias[rb], 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(p.aq[rb][1], b1, acc, 0, 0, 0);
+      logit[rb][c][b] = fmaf(fmaf(digits_value(acc), p.inv_q[rb], p.Zg[rb]), n16, 0.f);
     }
   }
   if (t0 + kGroup > t_end) {   // a group cut short by max_tokens: mask the tokens beyond it
@@ -794,9 +812,30 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
     const int n_simd = (C::kWaves - 1 - simd) / 4 + 1 - first_i;      // compute waves on this SIMD
     GroupBytes cur;
     const StageLane sl = stage_lane(lane);
-    for (int k = simd + 4 * (wave / 4 - first_i); k < n_k; k += 4 * n_simd) {
+    // This wave's last group, if it is one of the split's last four (those
+    // land when the stream ends and bound the kernel's end): its key (s, z)
+    // pairs are fetched now, straight into LDS, so that the query side of
+    // its scores is ready before the group itself lands.
+    const int k_first = simd + 4 * (wave / 4 - first_i);
+    const int k_last = (k_first < n_k) ? k_first + (n_k - 1 - k_first) / (4 * n_simd) * (4 * n_simd) : -1;
+    const bool late = k_last >= 0 && k_last + 4 >= n_k;
+    if (late) {
+      const uint8_t* src = group_block(k_last) + kStageKsz + 16 * sz_piece_slot(lane & 31);
+      if (lane < 32) lds_load16(src, sm.last_ksz[k_last & 3]);
+    }
+    for (int k = k_first; k < n_k; k += 4 * n_simd) {
       const int s = k % C::kRing;
       const int use = k / C::kRing;
+      QPrep<RB> qp;
+      const bool prepped = late && k == k_last;
+      if (prepped) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the fetch above
+        const uint8_t* buf = sm.last_ksz[k_last & 3];
+        u32x2 ksz[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) ksz[b] = *reinterpret_cast<const u32x2*>(buf + sl.ksz[b >> 1] - kStageKsz + 16 * b);
+        q_prep<G>(ksz, qv, fac, sm, cw, gl, n, qp);
+      }
       while (read_flag(&sm.filled[s], lane) <= use)
         __builtin_amdgcn_s_sleep(1);
       read_stage(cur, sm.ring[s], sl);
@@ -808,8 +847,9 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
       // on its SIMD finish groups that landed earlier: it is issued first.
       if (k + 4 >= n_k) __builtin_amdgcn_s_setprio(2);
       const int g = split + k * S;
+      if (!prepped) q_prep<G>(cur.ksz, qv, fac, sm, cw, gl, n, qp);
       float alpha[RB], inv_p[RB];
-      score_phase<G>(cur, g * kGroup, total, qv, fac, sm, st, cw, gl, n, alpha, inv_p);
+      score_phase<G>(cur, qp, g * kGroup, total, sm, st, cw, gl, n, fac, alpha, inv_p);
       value_phase<G>(cur, sm, st, cw, gl, n, alpha, inv_p);
     }
   }

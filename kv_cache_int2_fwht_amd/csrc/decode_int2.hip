@@ -165,18 +165,6 @@ static_assert(kStageV == 4096 && kStageKsz == 8192 && kStageVsz == kStageKsz + 5
 __device__ __forceinline__ int sz_piece_slot(int p) { return p ^ (((p >> 4) & 1) << 1); }   // an involution
 __device__ __forceinline__ int norm_piece_slot(int p) { return p ^ ((p >> 3) & 1); }        // an involution
 
-// One 16-byte-per-lane global -> LDS load: lane l's 16 bytes at gptr land at
-// LDS byte lds + 16 l (lanes switched off write nothing).  Issued as inline
-// assembly: the loader wave tracks completion with its own vector-memory
-// counter waits.  The cache is read once per step, so the loads carry the
-// nontemporal hint: a streaming probe of this access pattern runs at
-// 6.1 TB/s with it against 5.5 TB/s without.
-__device__ __forceinline__ void lds_load16(const void* gptr, const uint8_t* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(gptr), "s"(m0)
-               : "memory");
-}
-
 // Source byte offsets, inside a group block, of the 16 bytes a loader lane
 // copies with each of the group's load instructions (fixed for the kernel).
 struct LoaderLane {
@@ -209,29 +197,6 @@ __device__ __forceinline__ void dma_group(uint8_t* stage, const uint8_t* blk, co
   for (int j = 0; j < 4; ++j) lds_load16(blk + o.v[j], stage + kStageV + 1024 * j);
   lds_load16(blk + o.sz, stage + kStageKsz);
   if (lane < 16) lds_load16(blk + o.nrm, stage + kStageNorm);
-}
-
-// An LDS flag, read by lane 0 alone and broadcast to the wave (a read of
-// one word by all 64 lanes occupies the LDS longer).
-__device__ __forceinline__ int read_flag(const int* f, int lane) {
-  int v = 0;
-  if (lane == 0) v = __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-  return __builtin_amdgcn_readfirstlane(v);
-}
-
-// Wait until at most `rem` groups' copies of this wave are outstanding
-// (rem <= N; the counter wait takes its count as an immediate).
-template <int N>
-__device__ __forceinline__ void wait_groups_outstanding(int rem) {
-  if constexpr (N <= 0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  } else {
-    if (rem >= N) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N * kDmaPerGroup) : "memory");
-    } else {
-      wait_groups_outstanding<N - 1>(rem);
-    }
-  }
 }
 
 // Byte offsets inside a stage of the operands a lane reads (see the lane
@@ -733,7 +698,7 @@ __global__ __launch_bounds__(Int2Cfg<G>::kThreads) void decode_int2_kernel(Decod
       }
       // the counter wait is the release: the copies are in LDS before the
       // flag store issues (a release store would wait for every load)
-      wait_groups_outstanding<C::kAhead - 1>(issued - 1 - j);
+      wait_units_outstanding<kDmaPerGroup, C::kAhead - 1>(issued - 1 - j);
       const int k = wave + j * C::kLoaders;
       // one lane stores the flag (a store of all 64 lanes to one word would
       // occupy the LDS for many cycles)

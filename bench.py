@@ -498,25 +498,16 @@ def append_loop(args):
                 ob.quantize_kv(cache, cache.k_tail, cache.v_tail, start, one, 1)
             ob.decode_attn(cache, nq_dev[s], nt_dev[s], nq + nt, q_dev[s], sm, outs[s], ws)
 
-    # the append inside the decode launch: n_tail counts the new token (up to
-    # 128); a full tail is quantized after the step
-    plan_f, nq_f, nt_f = [], n_q0, tail0
-    for s in range(steps):
-        nt_f += 1
-        plan_f.append((nq_f, nt_f))
-        if nt_f == 128:
-            nq_f, nt_f = nq_f + 128, 0
-    nqf_dev = torch.tensor([[p[0]] for p in plan_f], dtype=torch.int32, device=dev)
-    ntf_dev = torch.tensor([[p[1]] for p in plan_f], dtype=torch.int32, device=dev)
+    # the append inside the decode launch (a DecodeSession: n_tail counts the
+    # new token, up to 128; a full tail is quantized after the step)
+    from kv_cache_int2_fwht_amd.session import DecodeSession
+    session = DecodeSession(cache, [n_q0], [tail0], Hq, steps, ws=ws)
     new_k = k_dev[0, :, L0:L0 + steps].transpose(0, 1).contiguous()[:, None]   # [steps, 1, H, 128]
     new_v = v_dev[0, :, L0:L0 + steps].transpose(0, 1).contiguous()[:, None]
 
     def loop_fused():
-        for s, (nq, nt) in enumerate(plan_f):
-            ob.decode_attn_append(cache, nqf_dev[s], ntf_dev[s], nq + nt, q_dev[s], new_k[s], new_v[s], sm, outs[s],
-                                  ws)
-            if nt == 128:
-                ob.quantize_kv(cache, cache.k_tail, cache.v_tail, start, one, 1)
+        for s in range(steps):
+            session.step(s, q_dev[s], new_k[s], new_v[s], sm, outs[s])
 
     def restore():
         for t, s0 in zip((cache.blocks, cache.k_tail, cache.v_tail), snapshot):

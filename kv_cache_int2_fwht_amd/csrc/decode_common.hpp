@@ -227,10 +227,19 @@ __device__ void bf16_tokens_wave(const uint16_t* k, const uint16_t* v, int n_tok
   // every load first: the query (A operand: head n, zero rows beyond G,
   // channels 32 ks + 8 gl .. +7), the key rows of the tiles (B operand) and
   // the value pairs of all tokens (lane = channel pair).  Tokens past n_tok
-  // read row 0 of the part and are discarded: their logits become -inf, and
-  // their value registers are set to 0, since the row may hold anything (a
-  // row past the tail that was never written, or the row into which another
-  // wave of this launch is storing the appended token) and 0 * NaN is NaN.
+  // are masked (logit -inf, weight 0) but still read a row, which must hold
+  // finite data (0 * NaN is NaN): row 0 of the part.  A token appended in
+  // this launch (row `last`) is read from its source rows k_last / v_last,
+  // since another wave may be storing it into the tail meanwhile; when that
+  // is row 0, the part holds no other valid token and all of its rows read
+  // the source rows (row stride 0).  One select per row keeps the address
+  // arithmetic, and so the register count, of the plain tail.
+  const bool own0 = k_last != nullptr && last == 0;
+  const int stride = own0 ? 0 : kHeadDim;
+  if (own0) {
+    k = k_last;
+    v = v_last;
+  }
   uint4 qa[4], kb[kTiles][4];
   uint32_t vv[kTailPart];
   {
@@ -240,17 +249,14 @@ __device__ void bf16_tokens_wave(const uint16_t* k, const uint16_t* v, int n_tok
 #pragma unroll
     for (int j = 0; j < kTiles; ++j) {
       const int tok = 16 * j + n;
-      const uint16_t* krow = (k_last != nullptr && tok == last) ? k_last
-                                                                : k + static_cast<size_t>(tok < n_tok ? tok : 0) * kHeadDim;
+      const uint16_t* krow = (k_last != nullptr && tok == last) ? k_last : k + (tok < n_tok ? tok : 0) * stride;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) kb[j][ks] = *reinterpret_cast<const uint4*>(krow + 32 * ks + 8 * gl);
     }
 #pragma unroll
     for (int e = 0; e < kTailPart; ++e) {
-      const uint16_t* vrow = (v_last != nullptr && e == last) ? v_last
-                                                               : v + static_cast<size_t>(e < n_tok ? e : 0) * kHeadDim;
-      const uint32_t x = *reinterpret_cast<const uint32_t*>(vrow + 2 * lane);
-      vv[e] = (e < n_tok) ? x : 0u;
+      const uint16_t* vrow = (v_last != nullptr && e == last) ? v_last : v + (e < n_tok ? e : 0) * stride;
+      vv[e] = *reinterpret_cast<const uint32_t*>(vrow + 2 * lane);
     }
   }
   // scores: tile j = tokens 16 j .. 16 j + 15; lane holds rows 4 gl + r of column n

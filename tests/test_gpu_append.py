@@ -58,23 +58,20 @@ def test_32k_append_inside_the_decode_launch(gpu_lib):
         o = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
         ob.decode_attn(ca, i32(nq), i32(nt), nq + nt, bits_to_dev_bf16(syn.query(w, 0, s)[None], dev), SM, o, ws)
         outs_a.append(o)
-    # the append inside the decode launch (the full tail is attended as bf16,
-    # then quantized after the step)
+    # the append inside the decode launch, driven by a DecodeSession (the full
+    # tail is attended as bf16, then quantized after the step)
+    from kv_cache_int2_fwht_amd.session import DecodeSession
     cb, outs_b = fresh(), []
-    nq, nt = n_q0, tail0
+    session = DecodeSession(cb, [n_q0], [tail0], Hq, steps, ws=ws)
     full_step = None
     for s in range(steps):
-        nt += 1
         o = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
         k_new = k_dev[0, :, L0 + s][None].contiguous()
         v_new = v_dev[0, :, L0 + s][None].contiguous()
-        ob.decode_attn_append(cb, i32(nq), i32(nt), nq + nt, bits_to_dev_bf16(syn.query(w, 0, s)[None], dev),
-                              k_new, v_new, SM, o, ws)
+        session.step(s, bits_to_dev_bf16(syn.query(w, 0, s)[None], dev), k_new, v_new, SM, o)
         outs_b.append(o)
-        if nt == 128:
+        if session.plans[s].full[0]:
             full_step = s
-            ob.quantize_kv(cb, cb.k_tail, cb.v_tail, i32(nq // 128), i32(1), 1)
-            nq, nt = nq + 128, 0
     torch.cuda.synchronize()
     assert full_step == 128 - tail0 - 1
     for s in range(steps):

@@ -119,27 +119,18 @@ def test_32k_append_in_decode_loop_graph_replay_matches_eager(gpu_lib):
     torch.cuda.synchronize()
     snapshot = {n: getattr(cache, n).clone() for n in STATE}
 
-    plan, n_quant, n_tail = [], n_q0, tail0
-    for s in range(steps):
-        n_tail += 1
-        plan.append((n_quant, n_tail))
-        if n_tail == 128:
-            n_quant, n_tail = n_quant + 128, 0
-    nq_dev = torch.tensor([[p[0]] for p in plan], dtype=torch.int32, device=dev)
-    nt_dev = torch.tensor([[p[1]] for p in plan], dtype=torch.int32, device=dev)
+    # the per-step counts live on the device before capture (DecodeSession)
+    from kv_cache_int2_fwht_amd.session import DecodeSession
+    session = DecodeSession(cache, [n_q0], [tail0], Hq, steps)
+    assert [s for s, p in enumerate(session.plans) if p.full[0]] == [70]
     q_dev = bits_to_dev_bf16(np.stack([syn.query(w, 0, s)[None] for s in range(steps)]), dev)
     new_k = k_dev[0, :, L0:L0 + steps].transpose(0, 1).contiguous()[:, None]   # [steps, 1, H, 128]
     new_v = v_dev[0, :, L0:L0 + steps].transpose(0, 1).contiguous()[:, None]
-    start = torch.full((1,), n_q0 // 128, dtype=torch.int32, device=dev)
-    one = torch.ones(1, dtype=torch.int32, device=dev)
     outs = torch.zeros((steps, B, Hq, 128), dtype=torch.float32, device=dev)
-    ws = ob.alloc_workspace(B, H, Hq, cap, device=dev)
 
     def loop():
-        for s, (nq, nt) in enumerate(plan):
-            ob.decode_attn_append(cache, nq_dev[s], nt_dev[s], nq + nt, q_dev[s], new_k[s], new_v[s], SM, outs[s], ws)
-            if nt == 128:
-                ob.quantize_kv(cache, cache.k_tail, cache.v_tail, start, one, 1)
+        for s in range(steps):
+            session.step(s, q_dev[s], new_k[s], new_v[s], SM, outs[s])
 
     def restore():
         for n in STATE:

@@ -26,20 +26,26 @@ namespace {
 constexpr int kThreads = 256;
 constexpr double kSqrt128 = 0x1.6a09e667f3bcdp+3;  // 8 * sqrt(2)
 
-__device__ __forceinline__ uint32_t code_from(double x, double z, double s, double inv_s) {
-  // inv_s == 0 encodes s == 0: r = 0 and the code is 0.
-  double r = (x - z) * inv_s;
-  // Within a hair of a half-way point the reciprocal product can land on the
-  // other side of an exact tie; decide those with the correctly rounded
-  // quotient.  Such values are rare, so the division runs only in waves that
-  // hold one.
-  const bool near_tie = fabs((r - floor(r)) - 0.5) < 1e-9 && s > 0.0;
-  if (__any(near_tie)) {
-    if (near_tie) r = (x - z) / s;
-  }
-  const double c = fmin(fmax(rint(r), 0.0), 3.0);
-  return static_cast<uint32_t>(c);
+// The code of x for the levels (z, s): clamp(rne((x - z) / s), 0, 3), with
+// the quotient taken as the product (x - z) * inv_s.  Within a hair of a
+// half-way point that product can land on the other side of an exact tie
+// than the correctly rounded quotient, so `near` reports a quotient within
+// 1e-9 of one (|r - rne(r)| > 0.5 - 1e-9); code_exact decides those.
+// inv_s == 0 encodes s == 0: r = 0, code 0, never near.
+__device__ __forceinline__ uint32_t code_fast(double x, double z, double inv_s, bool& near) {
+  const double r = (x - z) * inv_s;
+  const double t = rint(r);
+  near = fabs(r - t) > 0.5 - 1e-9;
+  return static_cast<uint32_t>(fmin(fmax(t, 0.0), 3.0));
 }
+__device__ __forceinline__ uint32_t code_exact(double x, double z, double s) {
+  return static_cast<uint32_t>(fmin(fmax(rint((x - z) / s), 0.0), 3.0));
+}
+
+// Keeps a rare branch a branch: without it the compiler computes the
+// division of every code and selects, which costs more than the rest of the
+// decision.
+__device__ __forceinline__ void rare_path() { asm volatile("" ::: "memory"); }
 
 // 32 channels 32L .. 32L+31 of one key row (bf16) -> the unnormalised
 // Walsh-Hadamard transform Y = sqrt(128) H k in fp64 across the four lanes
@@ -252,12 +258,24 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
     uint32_t words[4];
 #pragma unroll
     for (int wd = 0; wd < 4; ++wd) {
-      uint32_t acc = 0;
+      uint32_t acc = 0, near_mask = 0;
 #pragma unroll 4
       for (int e = 0; e < 16; ++e) {
         const int t = half * 64 + wd * 16 + e;
         const double v = static_cast<double>(bf16_to_f32(vr[t * kHeadDim + d]));
-        acc |= code_from(v, sm.vz[t], sm.vs[t], sm.vinv[t]) << (2 * e);
+        bool near;
+        acc |= code_fast(v, sm.vz[t], sm.vinv[t], near) << (2 * e);
+        near_mask |= static_cast<uint32_t>(near) << e;
+      }
+      if (__any(near_mask != 0)) {
+        rare_path();
+        for (int e = 0; e < 16; ++e) {
+          if ((near_mask >> e) & 1u) {
+            const int t = half * 64 + wd * 16 + e;
+            const double v = static_cast<double>(bf16_to_f32(vr[t * kHeadDim + d]));
+            acc = (acc & ~(3u << (2 * e))) | (code_exact(v, sm.vz[t], sm.vs[t]) << (2 * e));
+          }
+        }
       }
       words[wd] = acc;
     }
@@ -278,12 +296,25 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
       key_fwht(ksrc + static_cast<int64_t>(t) * a.st, L, rotate, x);   // bit-identical to the first pass
     }
     const double inv = sm.inv_n[t];
-    uint32_t w0 = 0, w1 = 0;
+    uint32_t w0 = 0, w1 = 0, near0 = 0, near1 = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int c0 = padc(32 * L + i), c1 = padc(32 * L + 16 + i);
-      w0 |= code_from(x[i] * inv, sm.zs[c0], sm.ss[c0], sm.inv_s[c0]) << (2 * i);
-      w1 |= code_from(x[16 + i] * inv, sm.zs[c1], sm.ss[c1], sm.inv_s[c1]) << (2 * i);
+      bool n0, n1;
+      w0 |= code_fast(x[i] * inv, sm.zs[c0], sm.inv_s[c0], n0) << (2 * i);
+      w1 |= code_fast(x[16 + i] * inv, sm.zs[c1], sm.inv_s[c1], n1) << (2 * i);
+      near0 |= static_cast<uint32_t>(n0) << i;
+      near1 |= static_cast<uint32_t>(n1) << i;
+    }
+    if (__any((near0 | near1) != 0)) {
+      rare_path();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int c0 = padc(32 * L + i), c1 = padc(32 * L + 16 + i);
+        if ((near0 >> i) & 1u) w0 = (w0 & ~(3u << (2 * i))) | (code_exact(x[i] * inv, sm.zs[c0], sm.ss[c0]) << (2 * i));
+        if ((near1 >> i) & 1u)
+          w1 = (w1 & ~(3u << (2 * i))) | (code_exact(x[16 + i] * inv, sm.zs[c1], sm.ss[c1]) << (2 * i));
+      }
     }
     *reinterpret_cast<uint2*>(sm.u.out_codes + OSCAR_BLOCK_K_CODES + t * 32 + 8 * L) = make_uint2(w0, w1);
   }

@@ -51,6 +51,9 @@ def test_quantize_matches_oracle(gpu_lib, cfg):
             rep = check_quantized_slice(cache, b, h, ref)
             exact += all(rep[key] for key in rep if key.endswith("equal"))
     _say(f"slices bit-identical to the oracle: {exact} of {w.batch * w.num_kv_heads}")
+    # the codes are decided in fp64 like the oracle's, with the correctly
+    # rounded quotient near a half-way point: every slice is bit-identical
+    assert exact == w.batch * w.num_kv_heads
 
 
 def test_quantize_strided_offsets_and_ragged_groups(gpu_lib):
@@ -131,3 +134,43 @@ def test_quantize_is_deterministic(gpu_lib):
     cache_a, k, v = _quantize_workload_on_gpu(ob, w, [1024], 1024, dev)
     cache_b, _, _ = _quantize_workload_on_gpu(ob, w, [1024], 1024, dev)
     assert torch.equal(cache_a.blocks, cache_b.blocks)
+
+
+def test_quantize_exact_half_way_values(gpu_lib):
+    """Values and keys exactly half-way between two code levels, where the
+    quantizer decides the code from the correctly rounded quotient instead
+    of the reciprocal product: every value token and every key channel holds
+    levels 0 and 3 (z = 0, s an exact power of two) and otherwise levels
+    from {0, 0.5, 1, ..., 3} times that power, so (x - z) / s lands exactly
+    on 0.5, 1.5 and 2.5 (round half to even: codes 0, 2, 2).  Keys are
+    quantized without rotation and scaling, the variant in which the codes
+    see the keys as given; the bytes must equal the oracle's bit for bit."""
+    from kv_cache_int2_fwht_amd import binding as ob
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(4242)
+    T = 256
+    levels = np.arange(7, dtype=np.float64) / 2.0               # 0, 0.5, ..., 3
+    lk = levels[rng.integers(0, 7, (T, 128))]
+    lv = levels[rng.integers(0, 7, (T, 128))]
+    for g in range(T // 128):                                    # per key group: each channel spans 0..3
+        lk[128 * g] = 0.0
+        lk[128 * g + 1] = 3.0
+    lv[:, 0] = 0.0                                               # per value token: 0..3
+    lv[:, 1] = 3.0
+    k = lk * np.exp2(rng.integers(-6, 4, (1, 128)))               # per-channel power of two
+    v = lv * np.exp2(rng.integers(-6, 4, (T, 1)))                 # per-token power of two
+    assert np.isin(lk, [0.5, 1.5, 2.5]).sum() > 1000 and np.isin(lv, [0.5, 1.5, 2.5]).sum() > 1000
+    kb, vb = syn.f32_to_bf16_bits(k.astype(np.float32)), syn.f32_to_bf16_bits(v.astype(np.float32))
+    assert np.array_equal(syn.bf16_bits_to_f64(kb), k) and np.array_equal(syn.bf16_bits_to_f64(vb), v)
+    flags = ob.KEYS_UNROTATED | ob.KEYS_UNSCALED
+    cache = ob.PackedCache(1, 1, T, device=dev, flags=flags)
+    _say("quantize exact half-way values (keys unrotated and unscaled)")
+    ob.quantize_kv(cache, bits_to_dev_bf16(kb, dev)[None, None], bits_to_dev_bf16(vb, dev)[None, None],
+                   torch.zeros(1, dtype=torch.int32, device=dev), torch.full((1,), T // 128, dtype=torch.int32,
+                                                                             device=dev), T // 128)
+    torch.cuda.synchronize()
+    ref = oracle.quantize_slice(syn.bf16_bits_to_f64(kb), syn.bf16_bits_to_f64(vb), T, keep_intermediates=True,
+                                rotate=False, scale=False)
+    rep = check_quantized_slice(cache, 0, 0, ref)
+    assert rep["key_code_mismatch"] == 0 and rep["value_code_mismatch"] == 0, rep
+    assert all(rep[key] for key in rep if key.endswith("equal")), rep

@@ -25,7 +25,7 @@ constexpr int kLoaders = 2;             // loader waves per workgroup
 constexpr int kAhead = 2;               // groups in flight per loader
 constexpr int kCopiesPerGroup = 10;     // 16-byte-per-lane copy instructions per group
 constexpr int kThreads = 1024;          // 16 waves, as the decode kernel for 4 query heads per KV head
-constexpr int kLdsBytes = 145732;       // the decode kernel's LDS footprint for 4 query heads per KV head
+constexpr int kLdsBytes = 147780;       // the decode kernel's LDS footprint for 4 query heads per KV head
 static_assert(kRing * kBlockBytes <= kLdsBytes, "ring fits");
 
 struct ProbeSmem {

@@ -215,16 +215,28 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
       hi = fmaxf(hi, dpp_f32<kDppRowRor4>(hi));
       lo = fminf(lo, dpp_f32<kDppRowRor8>(lo));
       hi = fmaxf(hi, dpp_f32<kDppRowRor8>(hi));
-      if (cb == 0) {
-        const uint16_t s_bits = f64_to_f16_bits_rne_sat((static_cast<double>(hi) - static_cast<double>(lo)) / 3.0);
-        const uint16_t z_bits = f64_to_f16_bits_rne_sat(static_cast<double>(lo));
-        reinterpret_cast<uint32_t*>(sm.out_params + (OSCAR_BLOCK_V_SZ - OSCAR_BLOCK_K_SZ))[t] =
-            static_cast<uint32_t>(s_bits) | (static_cast<uint32_t>(z_bits) << 16);
-        const double s16 = f16_bits_to_f64(s_bits);
-        sm.vz[t] = f16_bits_to_f64(z_bits);
-        sm.vs[t] = s16;
-        sm.vinv[t] = (s16 > 0.0) ? 1.0 / s16 : 0.0;
+      if (cb == 0) {   // the token's range, until its parameters are computed below
+        sm.vz[t] = static_cast<double>(lo);
+        sm.vs[t] = static_cast<double>(hi);
       }
+    }
+    // the parameters of the wave's 32 tokens, one per lane (computed once
+    // per pass with 4 lanes active, the divisions and fp16 roundings cost
+    // eight times as many instructions)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < 32) {
+      const int t = wave * 32 + lane;
+      const double lo = sm.vz[t], hi = sm.vs[t];
+      const uint16_t s_bits = f64_to_f16_bits_rne_sat((hi - lo) / 3.0);
+      const uint16_t z_bits = f64_to_f16_bits_rne_sat(lo);
+      reinterpret_cast<uint32_t*>(sm.out_params + (OSCAR_BLOCK_V_SZ - OSCAR_BLOCK_K_SZ))[t] =
+          static_cast<uint32_t>(s_bits) | (static_cast<uint32_t>(z_bits) << 16);
+      const double s16 = f16_bits_to_f64(s_bits);
+      sm.vz[t] = f16_bits_to_f64(z_bits);
+      sm.vs[t] = s16;
+      sm.vinv[t] = (s16 > 0.0) ? 1.0 / s16 : 0.0;
     }
   }
   __syncthreads();

@@ -78,18 +78,6 @@ __device__ void load_and_rotate_q(const uint16_t* q, float scale, float (*dst_ra
   rotate_q<G, kRows>(fetch_q<G, kRows>(q), scale, dst_raw, dst_rot);
 }
 
-// One 16-byte-per-lane global -> LDS load: lane l's 16 bytes at gptr land at
-// LDS byte lds + 16 l (lanes switched off write nothing).  Issued as inline
-// assembly: a loader wave tracks completion with its own vector-memory
-// counter waits.  The caches are read once per decode step, so the loads
-// carry the nontemporal hint (a streaming probe of the INT2 access pattern
-// runs at 6.1 TB/s with it against 5.5 TB/s without).
-__device__ __forceinline__ void lds_load16(const void* gptr, const uint8_t* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(gptr), "s"(m0)
-               : "memory");
-}
-
 // Wait until at most `rem` units of kPerUnit copies each of this wave are
 // outstanding (rem <= N; the counter wait takes its count as an immediate).
 template <int kPerUnit, int N>

@@ -50,12 +50,17 @@ __device__ __forceinline__ void rare_path() { asm volatile("" ::: "memory"); }
 // 32 channels 32L .. 32L+31 of one key row (bf16) -> the unnormalised
 // Walsh-Hadamard transform Y = sqrt(128) H k in fp64 across the four lanes
 // L = 0..3 of a quad: channel bits 0..4 in-lane, bits 5 and 6 across the
-// quad (exact for bf16 inputs in practice).
-__device__ __forceinline__ void key_fwht(const uint16_t* row, int L, bool rotate, double (&x)[32]) {
+// quad (exact for bf16 inputs in practice).  key_row_load fetches the lane's
+// 64 bytes of the row; key_fwht_raw transforms them.
+__device__ __forceinline__ void key_row_load(const uint16_t* row, int L, uint4 (&raw)[4]) {
   const uint4* src = reinterpret_cast<const uint4*>(row + 32 * L);
 #pragma unroll
+  for (int q = 0; q < 4; ++q) raw[q] = src[q];
+}
+__device__ __forceinline__ void key_fwht_raw(const uint4 (&raw)[4], int L, bool rotate, double (&x)[32]) {
+#pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint4 w = src[q];
+    const uint4 w = raw[q];
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -85,6 +90,11 @@ __device__ __forceinline__ void key_fwht(const uint16_t* row, int L, bool rotate
   for (int i = 0; i < 32; ++i) {
     x[i] = fma(s2, x[i], dpp_f64<kDppQuadXor2>(x[i]));
   }
+}
+__device__ __forceinline__ void key_fwht(const uint16_t* row, int L, bool rotate, double (&x)[32]) {
+  uint4 raw[4];
+  key_row_load(row, L, raw);
+  key_fwht_raw(raw, L, rotate, x);
 }
 
 // Per-channel LDS arrays are read and written by the four lanes of a quad
@@ -134,12 +144,25 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
 
   __shared__ QuantSmem sm;
 
+  // The memory reads first, so that they overlap the key transforms: the
+  // wave's 32 value rows straight into LDS (4 rows per wave instruction),
+  // then the key rows of both key passes into registers.
+  {
+    const uint16_t* vrows = vsrc + static_cast<int64_t>(wave * 32 + (lane >> 4)) * a.st + 8 * (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      lds_load16(vrows + static_cast<int64_t>(4 * i) * a.st, reinterpret_cast<const uint8_t*>(&sm.vrow[wave * 32 + 4 * i][0]));
+  }
+
   // ---------------- keys, first pass: norms and per-channel ranges ----------------
   // Lane = (slot, L): 4 lanes per token, lane L holds channels 32L..32L+31.
   // A wave covers 16 tokens per pass, two passes: tokens wave*32 + pass*16 + slot.
   const int L = lane & 3;
   const int slot = lane >> 2;
   const int row = wave * 4 + (lane >> 4);
+  uint4 kraw[2][4];
+  key_row_load(ksrc + static_cast<int64_t>(wave * 32 + slot) * a.st, L, kraw[0]);
+  key_row_load(ksrc + static_cast<int64_t>(wave * 32 + 16 + slot) * a.st, L, kraw[1]);
   // the first pass's transformed keys stay in registers until their codes
   // are decided after the block-wide reduction (the second pass's are
   // transformed again then: keeping both would not fit the registers)
@@ -148,7 +171,10 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
   for (int pass = 0; pass < 2; ++pass) {
     const int t = wave * 32 + pass * 16 + slot;
     double x[32];
-    key_fwht(ksrc + static_cast<int64_t>(t) * a.st, L, rotate, x);
+    uint4 raw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) raw[q] = pass ? kraw[1][q] : kraw[0][q];
+    key_fwht_raw(raw, L, rotate, x);
     if (pass == 0) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) xk[i] = x[i];
@@ -194,11 +220,12 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
   {
     const int cb = lane & 15;
     const int tslot = lane >> 4;
+    // the copies of the wave's value rows (issued first) have landed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll 2
     for (int pass = 0; pass < 8; ++pass) {
       const int t = wave * 32 + pass * 4 + tslot;
-      const uint4 w = *reinterpret_cast<const uint4*>(vsrc + static_cast<int64_t>(t) * a.st + 8 * cb);
-      sm.vrow[t][cb] = w;
+      const uint4 w = sm.vrow[t][cb];
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
       float lo = bf16lo_to_f32(ws[0]), hi = lo;
 #pragma unroll

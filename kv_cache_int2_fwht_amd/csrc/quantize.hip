@@ -11,12 +11,16 @@
 // KV head).  Every quantity that decides an fp16 parameter or a code is
 // computed in fp64: the Hadamard butterflies on bf16 inputs are then exact
 // in practice, so the stored norms, scales, zero-points and codes are the
-// ones an fp64 evaluation of the same formulas gives.  The keys are read
-// twice (the second time from cache): the first pass finds norms and
-// per-channel ranges, the second repeats the identical transform and writes
-// the codes, so no lane has to keep a whole token's fp64 row alive across
-// the block-wide reduction.  The group's values are kept in LDS between
-// their two passes.
+// ones an fp64 evaluation of the same formulas gives.  The memory reads are
+// issued first, so that they overlap the transforms: the group's value rows
+// straight into LDS (where they stay for both value passes), the key rows
+// into registers.  The first key pass finds norms and per-channel ranges;
+// after the block-wide reduction the second decides the codes, from the
+// first pass's transformed keys kept in registers for half of each wave's
+// tokens and from an identical transform repeated on the other half (read
+// again from cache: keeping both halves would not fit the registers).  A
+// code decision near a half-way point takes the correctly rounded division,
+// on a branch of its own.
 #include "device_common.hpp"
 #include "internal.hpp"
 

@@ -92,22 +92,24 @@ def test_32k_append_inside_the_decode_launch(gpu_lib):
         assert_out_close(got[h * G:(h + 1) * G], ref, f"full tail, head {h}")
 
 
+@pytest.mark.parametrize("G", [1, 4, 8])
 @pytest.mark.parametrize("n_tail", [1, 64, 65, 127, 128])
-def test_append_with_non_finite_rows_past_the_tail(gpu_lib, n_tail):
+def test_append_with_non_finite_rows_past_the_tail(gpu_lib, n_tail, G):
     """Tail rows past the appended token hold NaN (never written: the ABI does
     not ask the caller to initialise them).  Each tail wave reads masked
     tokens from a row of its own part, which at n_tail = 65 is the very row
     the other wave stores the new token into; none of it may reach the
-    output.  Two sequences of 512 quantized tokens, two KV heads of four
-    query heads each, against the oracle."""
+    output.  Two sequences of 512 quantized tokens, two KV heads of G query
+    heads each (G = 8: two row groups of the tail's matrix operand), against
+    the oracle."""
     from kv_cache_int2_fwht_amd import binding as ob
     from tests.helpers import upload_slice
     dev = torch.device("cuda:0")
-    Hkv, Hq = 2, 8
-    G = Hq // Hkv
+    Hkv = 2
+    Hq = G * Hkv
     nq = 512
-    w = syn.custom_workload(2, Hq, Hkv, [nq + n_tail, nq + n_tail], cfg_tag=120 + n_tail)
-    print(f"append with NaN past the tail: n_tail {n_tail}", flush=True)
+    w = syn.custom_workload(2, Hq, Hkv, [nq + n_tail, nq + n_tail], cfg_tag=120 + n_tail + (0 if G == 4 else 1000 * G))
+    print(f"append with NaN past the tail: n_tail {n_tail}, G {G}", flush=True)
     cache = ob.PackedCache(2, Hkv, nq + 128, device=dev)
     refs, k_new, v_new = {}, [], []
     for b in range(2):
@@ -138,7 +140,7 @@ def test_append_with_non_finite_rows_past_the_tail(gpu_lib, n_tail):
     for b in range(2):
         for h in range(Hkv):
             ref = refs[b, h].decode(syn.bf16_bits_to_f64(q_bits[b, h * G:(h + 1) * G]), SM)
-            assert_out_close(got[b, h * G:(h + 1) * G], ref, f"n_tail {n_tail}, sequence {b}, head {h}")
+            assert_out_close(got[b, h * G:(h + 1) * G], ref, f"n_tail {n_tail}, G {G}, sequence {b}, head {h}")
     # the stored tail rows are exactly the appended tokens
     np.testing.assert_array_equal(cache.k_tail[:, :, n_tail - 1].view(torch.int16).cpu().numpy().view(np.uint16),
                                   np.stack(k_new))

@@ -178,7 +178,12 @@ size_t oscar_decode_workspace_bytes(int32_t batch, int32_t num_kv_heads,
                                     int32_t num_q_heads, int32_t max_tokens);
 
 /*
- * oscar_decode_attn -- one decode step over the packed INT2 cache.
+ * oscar_decode_attn -- one decode step over the packed INT2 cache: the step
+ * whose speed the pages report against BF16 FlashDecoding-v2 (OScaR
+ * abstract, fugumt.com record, "Abstract"; ai-papers.net OScaR summary,
+ * section "実験結果"), with the keys as the summary's section "OScaRの提案手法"
+ * stores them (rotated, then scaled per token), so the query is rotated the
+ * same way.
  *
  * For every sequence b and query head j (KV head j / (num_q_heads /
  * num_kv_heads)): rotate q by the same Hadamard matrix, score each quantized
@@ -244,7 +249,9 @@ oscar_status oscar_decode_attn_append(const oscar_kv_cache* cache,
  * oscar_decode_attn_splits writes for this shape (0 for invalid shapes).
  *
  * oscar_decode_attn_splits -- the first kernel of oscar_decode_attn: same
- * arguments except out.  It writes, at the start of ws, the float records
+ * arguments except out.  The record format is this library's (the pages
+ * describe no kernel); the merge is the standard combination of partial
+ * softmax states.  It writes, at the start of ws, the float records
  * [batch][num_q_heads][S][132] (S = oscar_decode_num_splits(batch,
  * num_kv_heads, max_tokens)); record (b, j, r) = (m, l, unused, unused,
  * acc[128]) over the tokens of split r of sequence b, in base 2:
@@ -301,7 +308,8 @@ oscar_status oscar_decode_attn_noalloc(const oscar_kv_cache* cache,
 /*
  * oscar_decode_attn_bf16 -- the same decode step over unquantized bf16
  * keys and values: plain split-K flash-decoding, the counterpart of the
- * BF16 FlashDecoding-v2 baseline the pages compare against.
+ * BF16 FlashDecoding-v2 baseline the pages compare against (ai-papers.net
+ * OScaR summary, section "実験結果"; OScaR abstract).
  *
  * k, v    : bf16 [batch][num_kv_heads][capacity][128].
  * seq_len : device int32[batch]; tokens of sequence b, <= capacity

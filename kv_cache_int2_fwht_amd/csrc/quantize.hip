@@ -46,6 +46,31 @@ __device__ __forceinline__ uint32_t code_exact(double x, double z, double s) {
   return static_cast<uint32_t>(fmin(fmax(rint((x - z) / s), 0.0), 3.0));
 }
 
+// Minimum and maximum of values that are never signalling NaNs (results of
+// arithmetic, moved across lanes or through LDS): the instruction alone.
+// fmin / fmax would first copy each operand the compiler cannot prove quiet
+// through a quieting max (one more fp64 instruction per operand).
+__device__ __forceinline__ double min_q(double a, double b) {
+  double r;
+  asm("v_min_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ double max_q(double a, double b) {
+  double r;
+  asm("v_max_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float minf_q(float a, float b) {
+  float r;
+  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float maxf_q(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Keeps a rare branch a branch: without it the compiler computes the
 // division of every code and selects, which costs more than the rest of the
 // decision.
@@ -203,17 +228,18 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const double u = x[i] * inv;
-      double mn = fmin(u, dpp_f64<kDppRowRor4>(u));
-      double mx = fmax(u, dpp_f64<kDppRowRor4>(u));
-      mn = fmin(mn, dpp_f64<kDppRowRor8>(mn));
-      mx = fmax(mx, dpp_f64<kDppRowRor8>(mx));
+      const double u4 = dpp_f64<kDppRowRor4>(u);
+      double mn = min_q(u, u4);
+      double mx = max_q(u, u4);
+      mn = min_q(mn, dpp_f64<kDppRowRor8>(mn));
+      mx = max_q(mx, dpp_f64<kDppRowRor8>(mx));
       if ((lane & 15) < 4) {
         if (pass == 0) {
           sm.u.r.red_min[row][padc(32 * L + i)] = mn;
           sm.u.r.red_max[row][padc(32 * L + i)] = mx;
         } else {   // the same lane wrote these entries in the first pass
-          sm.u.r.red_min[row][padc(32 * L + i)] = fmin(sm.u.r.red_min[row][padc(32 * L + i)], mn);
-          sm.u.r.red_max[row][padc(32 * L + i)] = fmax(sm.u.r.red_max[row][padc(32 * L + i)], mx);
+          sm.u.r.red_min[row][padc(32 * L + i)] = min_q(sm.u.r.red_min[row][padc(32 * L + i)], mn);
+          sm.u.r.red_max[row][padc(32 * L + i)] = max_q(sm.u.r.red_max[row][padc(32 * L + i)], mx);
         }
       }
     }
@@ -235,17 +261,17 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float f0 = bf16lo_to_f32(ws[e]), f1 = bf16hi_to_f32(ws[e]);
-        lo = fminf(lo, fminf(f0, f1));
-        hi = fmaxf(hi, fmaxf(f0, f1));
+        lo = minf_q(lo, minf_q(f0, f1));
+        hi = maxf_q(hi, maxf_q(f0, f1));
       }
-      lo = fminf(lo, dpp_f32<kDppQuadXor1>(lo));
-      hi = fmaxf(hi, dpp_f32<kDppQuadXor1>(hi));
-      lo = fminf(lo, dpp_f32<kDppQuadXor2>(lo));
-      hi = fmaxf(hi, dpp_f32<kDppQuadXor2>(hi));
-      lo = fminf(lo, dpp_f32<kDppRowRor4>(lo));
-      hi = fmaxf(hi, dpp_f32<kDppRowRor4>(hi));
-      lo = fminf(lo, dpp_f32<kDppRowRor8>(lo));
-      hi = fmaxf(hi, dpp_f32<kDppRowRor8>(hi));
+      lo = minf_q(lo, dpp_f32<kDppQuadXor1>(lo));
+      hi = maxf_q(hi, dpp_f32<kDppQuadXor1>(hi));
+      lo = minf_q(lo, dpp_f32<kDppQuadXor2>(lo));
+      hi = maxf_q(hi, dpp_f32<kDppQuadXor2>(hi));
+      lo = minf_q(lo, dpp_f32<kDppRowRor4>(lo));
+      hi = maxf_q(hi, dpp_f32<kDppRowRor4>(hi));
+      lo = minf_q(lo, dpp_f32<kDppRowRor8>(lo));
+      hi = maxf_q(hi, dpp_f32<kDppRowRor8>(hi));
       if (cb == 0) {   // the token's range, until its parameters are computed below
         sm.vz[t] = static_cast<double>(lo);
         sm.vs[t] = static_cast<double>(hi);
@@ -278,8 +304,8 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kv_kernel(QuantizeArgs a
     double lo = sm.u.r.red_min[0][pt], hi = sm.u.r.red_max[0][pt];
 #pragma unroll
     for (int r = 1; r < 16; ++r) {
-      lo = fmin(lo, sm.u.r.red_min[r][pt]);
-      hi = fmax(hi, sm.u.r.red_max[r][pt]);
+      lo = min_q(lo, sm.u.r.red_min[r][pt]);
+      hi = max_q(hi, sm.u.r.red_max[r][pt]);
     }
     const uint16_t s_bits = f64_to_f16_bits_rne_sat((hi - lo) / 3.0);
     const uint16_t z_bits = f64_to_f16_bits_rne_sat(lo);

@@ -308,3 +308,30 @@ def test_merge_of_records_from_two_token_shards(gpu_lib):
     torch.cuda.synchronize()
     q = np.stack([syn.query(w, 0)])
     assert_out_close(out.cpu().numpy(), _oracle_out(w, full_slices, q, [n]), "two shards")
+
+
+@pytest.mark.parametrize("G", [4, 8])
+@pytest.mark.parametrize("max_tokens", [600, 1000, 1030])
+def test_int2_decode_max_tokens_cuts_the_sequences(gpu_lib, G, max_tokens):
+    """max_tokens below a sequence's length: only its first max_tokens
+    tokens are attended (quantized ones first, then the tail), so the cut can
+    fall inside a quantized group (the group's later tokens masked) or inside
+    the tail.  Sequence 0: 1024 quantized + 50 tail tokens; sequence 1: 512 +
+    100.  Reference: the oracle's dequantized tokens, truncated."""
+    from kv_cache_int2_fwht_amd import binding as ob
+    dev = torch.device("cuda:0")
+    Hkv = 2
+    w = syn.custom_workload(2, G * Hkv, Hkv, [1024 + 50, 512 + 100], cfg_tag=170 + G)
+    cache, slices, _, _, q, lens, nq = _build(ob, w, dev)
+    _say(f"max_tokens {max_tokens}, G {G}, lengths {lens}")
+    got, _ = _run_int2(ob, cache, q, lens, nq, dev, max_tokens=max_tokens)
+    assert np.isfinite(got).all()
+    for b in range(2):
+        m = min(max_tokens, lens[b])
+        for h in range(Hkv):
+            s = slices[b, h]
+            k_hat, v_hat = s.dequantized()
+            mq = min(m, s.n_quant)
+            ref = oracle.decode_slice(syn.bf16_bits_to_f64(q[b, h * G:(h + 1) * G]), k_hat[:mq], v_hat[:mq],
+                                      s.k_tail[:m - mq], s.v_tail[:m - mq], SM)
+            assert_out_close(got[b, h * G:(h + 1) * G], ref, f"max_tokens {max_tokens}, sequence {b}, head {h}")

@@ -335,3 +335,37 @@ def test_int2_decode_max_tokens_cuts_the_sequences(gpu_lib, G, max_tokens):
             ref = oracle.decode_slice(syn.bf16_bits_to_f64(q[b, h * G:(h + 1) * G]), k_hat[:mq], v_hat[:mq],
                                       s.k_tail[:m - mq], s.v_tail[:m - mq], SM)
             assert_out_close(got[b, h * G:(h + 1) * G], ref, f"max_tokens {max_tokens}, sequence {b}, head {h}")
+
+
+@pytest.mark.parametrize("max_tokens", [600, 1000, 1030])
+def test_bf16_decode_max_tokens_cuts_the_sequences(gpu_lib, max_tokens):
+    """The bf16 reference kernel with max_tokens below a sequence's length
+    (a cut inside a 32-token piece): only the first max_tokens tokens are
+    attended."""
+    from kv_cache_int2_fwht_amd import binding as ob
+    dev = torch.device("cuda:0")
+    B, H, G = 2, 2, 4
+    w = syn.custom_workload(B, G * H, H, [1024 + 50, 512 + 100], cfg_tag=180)
+    lens = [w.total_tokens(b) for b in range(B)]
+    cap = max(lens)
+    k = np.zeros((B, H, cap, 128), np.uint16)
+    v = np.zeros((B, H, cap, 128), np.uint16)
+    for b in range(B):
+        for h in range(H):
+            k[b, h, :lens[b]] = syn.keys_slice(w, b, h)
+            v[b, h, :lens[b]] = syn.values_slice(w, b, h)
+    q = np.stack([syn.query(w, b) for b in range(B)])
+    _say(f"bf16 decode, max_tokens {max_tokens}, lengths {lens}")
+    out = torch.empty((B, G * H, 128), dtype=torch.float32, device=dev)
+    ws = ob.alloc_workspace(B, H, G * H, max_tokens, device=dev)
+    ob.decode_attn_bf16(bits_to_dev_bf16(k, dev), bits_to_dev_bf16(v, dev),
+                        torch.tensor(lens, dtype=torch.int32, device=dev), max_tokens,
+                        bits_to_dev_bf16(q, dev), SM, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        m = min(max_tokens, lens[b])
+        for h in range(H):
+            ref = oracle.decode_bf16_slice(syn.bf16_bits_to_f64(q[b, h * G:(h + 1) * G]),
+                                           syn.bf16_bits_to_f64(k[b, h, :m]), syn.bf16_bits_to_f64(v[b, h, :m]), SM)
+            assert_out_close(got[b, h * G:(h + 1) * G], ref, f"bf16, max_tokens {max_tokens}, sequence {b}, head {h}")

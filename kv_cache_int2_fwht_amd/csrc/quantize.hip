@@ -46,10 +46,11 @@ __device__ __forceinline__ uint32_t code_exact(double x, double z, double s) {
   return static_cast<uint32_t>(fmin(fmax(rint((x - z) / s), 0.0), 3.0));
 }
 
-// Minimum and maximum of values that are never signalling NaNs (results of
-// arithmetic, moved across lanes or through LDS): the instruction alone.
-// fmin / fmax would first copy each operand the compiler cannot prove quiet
-// through a quieting max (one more fp64 instruction per operand).
+// Minimum and maximum as the bare instructions.  fmin / fmax would first
+// copy each operand the compiler cannot prove quiet (results of cross-lane
+// moves, LDS loads and bit conversions) through a quieting max, one more
+// instruction per operand.  The two agree on every input that is not a
+// NaN; inputs holding NaN have no defined parameters either way.
 __device__ __forceinline__ double min_q(double a, double b) {
   double r;
   asm("v_min_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
